@@ -1,0 +1,149 @@
+"""W8A8 FP8 linear layer, step by step on the CPU (oracle; tests only).
+
+The method, from the pages:
+  * "Prototype FP8Linear W8A8 runtime quantization", opening post: both the
+    weights and the activations are quantized to float8_e4m3fn at run time and
+    an FP8 W8A8 GEMM multiplies them.
+  * "Fp8 Quantization Support", description and recipe: symmetric (no zero
+    point) float quantization, one scale per tensor for weights and input
+    activations; a float format's range and rounding differ from int8's.
+  * "[Kernel] Implement fallback for FP8 channelwise using torch._scaled_mm",
+    description: channelwise weights (one scale per output channel) are
+    served by a per-tensor scaled GEMM followed by a rescale of each output
+    column.
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes): the dynamic scale is amax/448 rounded once to float32, with
+amax == 0 mapping to scale 1.0; values are divided (not multiplied by a
+reciprocal) in float32; the cast saturates and rounds to nearest even; the
+weight has nn.Linear layout [N, K] and output channel n is weight row n; an
+optional bias is added after scaling.
+
+Precision: the quantization steps are float32, as the GPU computes them, so
+that both sides take every rounding decision in the same precision.  The GEMM
+is exact (fp64 of decoded e4m3 values is exact for K < 171,196; int64 is exact
+always), and the epilogue is fp64 and left unrounded.
+"""
+import numpy as np
+
+from .e4m3 import E4M3_MAX, decode, encode
+
+_F32_MAX = np.float32(E4M3_MAX)
+
+
+def bf16_bits_to_f32(bits):
+    """bf16 bit patterns (uint16) -> float32; exact (the bits move up 16)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32)
+
+
+def amax(x_f32):
+    """max |x| over the whole array as float32 (0 for an empty array)."""
+    x_f32 = np.asarray(x_f32, dtype=np.float32)
+    if x_f32.size == 0:
+        return np.float32(0.0)
+    return np.float32(np.max(np.abs(x_f32)))
+
+
+def scale_from_amax(a):
+    """Per-tensor scale mapping amax onto the e4m3fn maximum 448.
+
+    s = fl32(amax / 448) (one correctly rounded float32 division); an
+    all-zero (or empty) tensor has no range to map and takes s = 1.
+    """
+    a = np.float32(a)
+    if a == 0:
+        return np.float32(1.0)
+    return np.float32(a / _F32_MAX)
+
+
+def quant_static(x_bits, scale):
+    """Quantize bf16 bits with a given float32 scale: enc(fl32(x / scale)).
+
+    The division is float32 and correctly rounded, then the saturating RNE
+    encoder runs on that float32 quotient.
+    """
+    x = bf16_bits_to_f32(x_bits)
+    s = np.float32(scale)
+    with np.errstate(over="ignore", divide="ignore", invalid="ignore"):
+        v = (x / s).astype(np.float32)
+    return encode(v)
+
+
+def quant_dynamic(x_bits):
+    """Dynamic per-tensor activation quantization: returns (codes, scale)."""
+    x = bf16_bits_to_f32(x_bits)
+    s = scale_from_amax(amax(x))
+    return quant_static(x_bits, s), s
+
+
+def quant_weight(w_bits, per_channel):
+    """Weight quantization, [N, K] bf16 bits -> (codes [N, K], scales).
+
+    Per tensor: one scale from the amax of the whole matrix (shape [1]).
+    Per channel: row n (output channel n) gets its own scale from its own
+    amax (shape [N]); an all-zero row gets scale 1.
+    """
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    if not per_channel:
+        q, s = quant_dynamic(w_bits)
+        return q, np.array([s], dtype=np.float32)
+    n = w_bits.shape[0]
+    q = np.empty(w_bits.shape, dtype=np.uint8)
+    s = np.empty(n, dtype=np.float32)
+    for i in range(n):
+        q[i], s[i] = quant_dynamic(w_bits[i])
+    return q, s
+
+
+def gemm_exact(a_q, w_q):
+    """acc[m, n] = sum_k dec(A_q[m, k]) * dec(W_q[n, k]), exactly.
+
+    Every decoded value times 512 is an integer, so each product is an
+    integer multiple of 2^-18 below 448^2 and the float64 sum of K of them is
+    exact while K * 448^2 * 2^18 < 2^53, i.e. K < 171,196.
+    """
+    a_q = np.asarray(a_q, dtype=np.uint8)
+    w_q = np.asarray(w_q, dtype=np.uint8)
+    k = a_q.shape[1]
+    if k >= 171196:
+        raise ValueError("K too large for the exact float64 path")
+    return decode(a_q) @ decode(w_q).T
+
+
+def scaled_mm(a_q, w_q, s_a, s_w, per_channel, bias_bits=None, acc=None):
+    """The rescale epilogue in float64, unrounded.
+
+    out[m, n] = acc[m, n] * s_a * s_w[n] (+ bias[n]); per tensor uses s_w[0]
+    for every column.  Because s_w[n] does not vary along k, this equals a
+    per-tensor scaled GEMM followed by a rescale of column n.
+    """
+    if acc is None:
+        acc = gemm_exact(a_q, w_q)
+    s_w = np.asarray(s_w, dtype=np.float32).astype(np.float64)
+    col = s_w if per_channel else np.full(acc.shape[1], s_w[0])
+    out = acc * np.float64(np.float32(s_a)) * col[None, :]
+    if bias_bits is not None:
+        out = out + bf16_bits_to_f32(bias_bits).astype(np.float64)[None, :]
+    return out
+
+
+def dequant_row_norms(q, scales, per_row):
+    """L2 norm of each dequantized row: ||dec(q[r, :]) * scale_r||_2 (fp64)."""
+    d = decode(np.asarray(q, dtype=np.uint8))
+    s = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    s = s if per_row else np.full(d.shape[0], s.reshape(-1)[0])
+    return np.sqrt(np.sum(d * d, axis=1)) * np.abs(s)
+
+
+def to_bf16_rne(x):
+    """Round float64 values to the nearest bfloat16 (ties to even); float64.
+
+    bfloat16 keeps 8 significant bits; below 2^-126 its step is 2^-133.
+    Used only to report what an ideal bf16 output would be.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                       # x = m * 2^e, 0.5 <= |m| < 1
+    q = np.ldexp(1.0, np.maximum(e - 8, -133))
+    r = np.rint(x / q) * q                    # x / q is exact (power of two)
+    return np.where(x == 0, x, r)

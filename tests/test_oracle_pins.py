@@ -1,0 +1,320 @@
+"""Pins of the CPU oracle to facts fixed outside it (no GPU needed).
+
+Each test fixes the oracle against a closed form, an exhaustive brute force, a
+library routine, or an invariant of the method, chosen so that a plausible
+slip (wrong bias, sign, tie rule, dropped scale, transposed operand) fails.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import e4m3
+from fp8_w8a8_quantized_amd import synth
+
+ALL_BYTES = np.arange(256, dtype=np.uint8)
+ALL_BF16 = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+
+
+# ---------------------------------------------------------------- O-P1 decode
+def test_decode_spot_values():
+    d = oracle.decode(np.array([0x7E, 0x01, 0x08, 0x38, 0x00, 0x77, 0xFE, 0x07, 0x09], np.uint8))
+    assert d.tolist() == [448.0, 2.0 ** -9, 2.0 ** -6, 1.0, 0.0, 240.0, -448.0, 7 * 2.0 ** -9, 1.125 * 2.0 ** -6]
+    assert np.isnan(oracle.decode(np.array([0x7F, 0xFF], np.uint8))).all()
+    neg0 = oracle.decode(np.array([0x80], np.uint8))[0]
+    assert neg0 == 0.0 and np.signbit(neg0)
+
+
+def test_decode_table_matches_torch_float8_e4m3fn():
+    ours = oracle.decode(ALL_BYTES)
+    theirs = torch.from_numpy(ALL_BYTES.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(theirs))
+    fin = ~np.isnan(ours)
+    assert np.array_equal(ours[fin], theirs[fin])
+    assert np.array_equal(np.signbit(ours[fin]), np.signbit(theirs[fin]))
+
+
+def test_decode_table_shape_of_format():
+    g = oracle.positive_grid()
+    assert len(g) == 127 and g[0] == 0.0 and g[-1] == 448.0
+    assert np.all(np.diff(g) > 0)
+    # uniform 2^-9 spacing through the subnormals into the first binade
+    assert np.all(np.diff(g[:17]) == 2.0 ** -9)
+    vals = oracle.decode(ALL_BYTES)
+    assert len(np.unique(vals[~np.isnan(vals)])) == 253
+    assert np.sum(np.isnan(vals)) == 2
+
+
+# ------------------------------------------------------------ O-P2 round trip
+def test_encode_decode_round_trip_all_patterns():
+    vals = oracle.decode(ALL_BYTES).astype(np.float32)
+    codes = oracle.encode(vals)
+    nan = np.isnan(vals)
+    assert np.array_equal(codes[~nan], ALL_BYTES[~nan])
+    assert np.all((codes[nan] & 0x7F) == 0x7F)
+
+
+# ---------------------------------------------- O-P3 exhaustive bf16, brute force
+def _bitwise_encoder(v):
+    """Independent e4m3fn encoder on the float32 bits (integer RNE)."""
+    u = np.asarray(v, np.float32).view(np.uint32).astype(np.int64)
+    sign = (u >> 24) & 0x80
+    a = u & 0x7FFFFFFF
+    exp = a >> 23
+    mant = (a & 0x7FFFFF) | np.where(exp > 0, 1 << 23, 0)
+    # value = mant * 2^(max(exp,1) - 150); target quantum 2^(max(e,-6) - 3)
+    e_unb = np.maximum(exp, 1) - 127
+    qexp = np.maximum(e_unb, -6) - 3
+    shift = qexp - (np.maximum(exp, 1) - 150)          # bits to drop, >= 20
+    shift = np.minimum(shift, 62)
+    kept = mant >> shift
+    rem = mant - (kept << shift)
+    half = np.int64(1) << (shift - 1)
+    up = (rem > half) | ((rem == half) & ((kept & 1) == 1))
+    n = kept + up                                       # value = n * 2^qexp
+    # code from (n, qexp): subnormal region qexp == -9 has code n directly
+    code = np.where(qexp == -9, n, ((qexp + 3 + 7) << 3) + (n - 8))
+    code = np.minimum(code, 0x7E)
+    code = np.where(a > 0x7F800000, 0x7F, np.where(a == 0x7F800000, 0x7E, code))
+    return (code | sign).astype(np.uint8)
+
+
+def test_encode_all_bf16_patterns_bitwise_and_brute_force():
+    x = oracle.bf16_bits_to_f32(ALL_BF16)
+    codes = oracle.quant_static(ALL_BF16, np.float32(1.0))
+    assert np.array_equal(codes, _bitwise_encoder(x))
+    # brute force: nearest of the finite grid, ties to even code, saturation
+    fin = np.isfinite(x)
+    a = np.abs(x[fin].astype(np.float64))
+    grid = oracle.positive_grid()
+    dist = np.abs(a[:, None] - grid[None, :])
+    best = dist.min(axis=1, keepdims=True)
+    cand = dist == best
+    n_cand = cand.sum(axis=1)
+    first = cand.argmax(axis=1)
+    last = 126 - cand[:, ::-1].argmax(axis=1)
+    pick = np.where(n_cand == 1, first, np.where(first % 2 == 0, first, last))
+    pick = np.where(a > 448.0, 126, pick)
+    expect = pick.astype(np.uint8) | (np.signbit(x[fin]).astype(np.uint8) << 7)
+    assert np.array_equal(codes[fin], expect)
+
+
+def test_encode_specific_roundings():
+    v = np.array([448, 464, 465, 500, -500, 1.0625, 1.1875, 2 ** -10, 1.5 * 2 ** -10,
+                  -0.0, -1e-9, 2 ** -9 * 7.5, 2 ** -9 * 8.5, 3e38, -np.inf], dtype=np.float32)
+    got = oracle.encode(v).tolist()
+    assert got == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0x38, 0x3A, 0x00, 0x01,
+                   0x80, 0x80, 0x08, 0x08, 0x7E, 0xFE]
+
+
+# ------------------------------------------- O-P4 torch CPU saturating cast
+def test_encode_matches_torch_clamped_cast_on_random_float32():
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 2 ** 32, size=400_000, dtype=np.uint64).astype(np.uint32)
+    v = bits.view(np.float32)
+    v = v[np.isfinite(v)]
+    # add values crowded around e4m3 rounding midpoints
+    g = oracle.positive_grid()
+    mids = ((g[:-1] + g[1:]) / 2).astype(np.float32)
+    near = np.concatenate([np.nextafter(mids, 0), mids, np.nextafter(mids, 1000)]).astype(np.float32)
+    v = np.concatenate([v, near, -near, rng.standard_normal(100_000).astype(np.float32) * 100])
+    ours = oracle.encode(v)
+    t = torch.from_numpy(v).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, t)
+
+
+# ------------------------------------------------------------ scale rule (a2)
+def _nearest_f32_to(q):
+    """Correctly rounded float32 of a positive Fraction, by neighbour search."""
+    f = np.float32(float(q))   # within an ulp; fix up with exact comparisons
+    for _ in range(3):
+        lo, hi = np.nextafter(f, np.float32(0)), np.nextafter(f, np.float32(np.inf))
+        cands = [lo, f, hi]
+        errs = [abs(Fraction(float(c)) - q) for c in cands]
+        best = min(errs)
+        ties = [c for c, e in zip(cands, errs) if e == best]
+        f = ties[0] if len(ties) == 1 else [c for c in ties if (c.view(np.uint32) & 1) == 0][0]
+    return f
+
+
+def test_scale_is_correctly_rounded_amax_over_448():
+    rng = np.random.default_rng(3)
+    for a in list(rng.lognormal(0, 6, size=300).astype(np.float32)) + [np.float32(448.0), np.float32(1e-30)]:
+        s = oracle.scale_from_amax(a)
+        assert s.dtype == np.float32
+        assert s == _nearest_f32_to(Fraction(float(a)) / 448)
+    assert oracle.scale_from_amax(np.float32(0)) == np.float32(1.0)
+    assert oracle.scale_from_amax(np.float32(448)) == np.float32(1.0)
+
+
+def test_quotient_rounds_to_float32_before_encoding():
+    """x / s is one float32 rounding, then the e4m3 rounding (double rounding)."""
+    rng = np.random.default_rng(11)
+    x_bits = synth.f32_to_bf16_bits(rng.standard_normal(2000).astype(np.float32) * 3)
+    s = np.float32(0.0137)
+    x = oracle.bf16_bits_to_f32(x_bits)
+    q = oracle.quant_static(x_bits, s)
+    for xi, qi in zip(x[:300], q[:300]):
+        v = _nearest_f32_to(abs(Fraction(float(xi)) / Fraction(float(s)))) if xi != 0 else np.float32(0)
+        v = -v if xi < 0 else v
+        assert oracle.encode(np.array([v], np.float32))[0] == qi
+
+
+# ----------------------------------------------- O-P6 dynamic-quant invariants
+def test_dynamic_quant_invariants():
+    x_bits = synth.activations(1, 16, 512, outliers=True)
+    q, s = oracle.quant_dynamic(x_bits)
+    x = oracle.bf16_bits_to_f32(x_bits)
+    i = np.unravel_index(np.argmax(np.abs(x)), x.shape)
+    assert q[i] in (0x7E, 0xFE)
+    assert np.max(np.abs(oracle.decode(q))) == 448.0
+    # sign symmetry: x -> -x flips only bit 7 of every code
+    qn, sn = oracle.quant_dynamic(x_bits ^ np.uint16(0x8000))
+    assert sn == s and np.array_equal(qn, q ^ np.uint8(0x80))
+    # power-of-two scaling: same codes, scale times exactly 2^j
+    for j in (-5, -1, 1, 4):
+        xs = synth.f32_to_bf16_bits(x * np.float32(2.0 ** j))
+        qj, sj = oracle.quant_dynamic(xs)
+        assert np.array_equal(qj, q) and sj == np.float32(s * 2.0 ** j)
+
+
+def test_dynamic_quant_zero_and_empty():
+    q, s = oracle.quant_dynamic(np.zeros((3, 5), np.uint16))
+    assert s == 1.0 and np.all(q == 0)
+    q, s = oracle.quant_dynamic(np.full((2, 2), 0x8000, np.uint16))
+    assert s == 1.0 and np.all(q == 0x80)
+    q, s = oracle.quant_dynamic(np.zeros((0, 7), np.uint16))
+    assert s == 1.0 and q.shape == (0, 7)
+
+
+def test_weight_quant_per_channel_rows_independent():
+    w = synth.weights(2, 24, 96, row_multipliers=True)
+    q, s = oracle.quant_weight(w, per_channel=True)
+    assert s.shape == (24,) and q.shape == (24, 96) and q.dtype == np.uint8
+    for n in (0, 7, 23):
+        qn, sn = oracle.quant_dynamic(w[n:n + 1])
+        assert sn == s[n] and np.array_equal(qn[0], q[n])
+    w0 = w.copy(); w0[5] = 0
+    q0, s0 = oracle.quant_weight(w0, per_channel=True)
+    assert s0[5] == 1.0 and np.all(q0[5] == 0)
+    qt, st = oracle.quant_weight(w, per_channel=False)
+    assert st.shape == (1,) and np.max(np.abs(oracle.decode(qt))) == 448.0
+
+
+# ----------------------------------------------------- O-P7 exact accumulation
+def test_gemm_exact_equals_int64_and_naive_loops():
+    rng = np.random.default_rng(5)
+    finite = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], np.uint8)
+    for (m, n, k) in [(1, 1, 1), (3, 5, 7), (8, 8, 8), (4, 6, 200)]:
+        a = rng.choice(finite, size=(m, k)); w = rng.choice(finite, size=(n, k))
+        acc = oracle.gemm_exact(a, w)
+        ai = np.rint(oracle.decode(a) * 512).astype(np.int64)
+        wi = np.rint(oracle.decode(w) * 512).astype(np.int64)
+        acc_int = ai @ wi.T
+        assert np.array_equal(acc, acc_int.astype(np.float64) * 2.0 ** -18)
+        if k <= 8:
+            da, dw = oracle.decode(a), oracle.decode(w)
+            for i in range(m):
+                for j in range(n):
+                    tot = Fraction(0)
+                    for kk in range(k):
+                        tot += Fraction(float(da[i, kk])) * Fraction(float(dw[j, kk]))
+                    assert Fraction(float(acc[i, j])) == tot
+
+
+def test_gemm_exact_worst_case_magnitude_stays_exact():
+    k = 14336
+    a = np.full((1, k), 0x7E, np.uint8); w = np.full((2, k), 0x7E, np.uint8)
+    w[1, ::2] = 0xFE
+    acc = oracle.gemm_exact(a, w)
+    assert acc[0, 0] == 448.0 * 448.0 * k and acc[0, 1] == 0.0
+
+
+# ------------------------------------------------- O-P8 closed-form special cases
+def test_k1_and_identity_weight_closed_forms():
+    a_bits = synth.activations(1, 4, 1); w_bits = synth.weights(1, 3, 1)
+    b_bits = synth.bias(1, 3)
+    aq, sa = oracle.quant_dynamic(a_bits); wq, sw = oracle.quant_weight(w_bits, False)
+    out = oracle.scaled_mm(aq, wq, sa, sw, False, b_bits)
+    bias = oracle.bf16_bits_to_f32(b_bits).astype(np.float64)
+    for i in range(4):
+        for j in range(3):
+            want = oracle.decode(aq[i:i + 1, 0])[0] * oracle.decode(wq[j:j + 1, 0])[0] * float(sa) * float(sw[0]) + bias[j]
+            assert out[i, j] == want
+    k = 32
+    aq, sa = oracle.quant_dynamic(synth.activations(1, 5, k))
+    eye = np.where(np.eye(k, dtype=bool), np.uint8(0x38), np.uint8(0))
+    sw = np.array([0.75], np.float32)
+    out = oracle.scaled_mm(aq, eye, sa, sw, False)
+    assert np.array_equal(out, oracle.decode(aq) * float(sa) * 0.75)
+    # a transposed operand would break this non-square case
+    eye_rect = eye[:20]
+    out = oracle.scaled_mm(aq, eye_rect, sa, sw, False)
+    assert np.array_equal(out, oracle.decode(aq)[:, :20] * float(sa) * 0.75)
+
+
+# ------------------------------------------- O-P9 / O-P10 channelwise factorization
+def test_per_channel_equal_scales_is_per_tensor_bit_exact():
+    aq, sa = oracle.quant_dynamic(synth.activations(2, 6, 64))
+    wq, _ = oracle.quant_weight(synth.weights(2, 10, 64), False)
+    sig = np.float32(0.0123)
+    per_t = oracle.scaled_mm(aq, wq, sa, np.array([sig]), False)
+    per_c = oracle.scaled_mm(aq, wq, sa, np.full(10, sig), True)
+    assert np.array_equal(per_t, per_c)
+
+
+def test_per_channel_is_per_tensor_gemm_then_column_rescale():
+    aq, sa = oracle.quant_dynamic(synth.activations(2, 6, 128, outliers=True))
+    wq, sw = oracle.quant_weight(synth.weights(2, 12, 128, row_multipliers=True), True)
+    per_c = oracle.scaled_mm(aq, wq, sa, sw, True)
+    unit = oracle.scaled_mm(aq, wq, sa, np.array([1.0], np.float32), False)
+    assert np.allclose(per_c, unit * sw.astype(np.float64)[None, :], rtol=1e-15, atol=0)
+    # the scale belongs to output column n = weight row n: check elements from
+    # the definition sum_k (s_a * A[m, k]) * (s_w[n] * W[n, k]) in exact rationals
+    da, dw = oracle.decode(aq), oracle.decode(wq)
+    for (m, n) in [(0, 0), (5, 11), (2, 7)]:
+        tot = sum(Fraction(float(da[m, k])) * Fraction(float(dw[n, k])) for k in range(128))
+        want = tot * Fraction(float(sa)) * Fraction(float(sw[n]))
+        assert abs(Fraction(float(per_c[m, n])) - want) <= abs(want) * Fraction(1, 2 ** 50)
+
+
+# ----------------------------------------------------- O-P11 tolerance reachable
+def test_tolerance_met_by_a_float32_blocked_accumulator():
+    """An fp32 kernel (128-wide k blocks, bf16 output) meets the element bound."""
+    k = 4096
+    a_bits = synth.activations(2, 16, k, outliers=True)
+    w_bits = synth.weights(2, 64, k, row_multipliers=True)
+    aq, sa = oracle.quant_dynamic(a_bits); wq, sw = oracle.quant_weight(w_bits, True)
+    ref = oracle.scaled_mm(aq, wq, sa, sw, True)
+    da = oracle.decode(aq).astype(np.float32); dw = oracle.decode(wq).astype(np.float32)
+    acc = np.zeros((16, 64), np.float32)
+    for k0 in range(0, k, 128):
+        acc = (acc + da[:, k0:k0 + 128] @ dw[:, k0:k0 + 128].T).astype(np.float32)
+    out = acc * (np.float32(sa) * sw[None, :])
+    out_bf16 = synth.f32_to_bf16_bits(out)
+    out_f = oracle.bf16_bits_to_f32(out_bf16).astype(np.float64)
+    bound = 1e-2 * np.outer(oracle.dequant_row_norms(aq, [sa], False), oracle.dequant_row_norms(wq, sw, True))
+    err = np.abs(out_f - ref)
+    assert np.all(err <= bound / 10)
+    big = np.abs(ref) > 1e-3
+    assert np.all(err[big] / np.abs(ref[big]) <= 2e-2)
+
+
+# ------------------------------------------------------------- O-P12 memory
+def test_one_byte_per_weight():
+    w = synth.weights(4, 1030, 96)
+    q, s = oracle.quant_weight(w, False)
+    assert q.nbytes == 1030 * 96 and s.nbytes == 4
+    q, s = oracle.quant_weight(w, True)
+    assert q.nbytes == 1030 * 96 and s.nbytes == 4 * 1030
+
+
+def test_bf16_rounding_helper():
+    v = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1 + 2 ** -9, 2.0 ** -130 * 1.5, -3.0000001])
+    r = oracle.to_bf16_rne(v)
+    assert r.tolist() == [1.0, 1.0, 1.0 + 4 * 2 ** -8, 1.0, 2.0 ** -130 * 1.5, -3.0]
+    x = np.random.default_rng(1).standard_normal(1000).astype(np.float32)
+    assert np.array_equal(oracle.to_bf16_rne(x.astype(np.float64)),
+                          oracle.bf16_bits_to_f32(synth.f32_to_bf16_bits(x)).astype(np.float64))
