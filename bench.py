@@ -1,0 +1,218 @@
+"""Benchmark of the FP8 W8A8 linear layer on one MI355X.
+
+One step = the whole hot path over one batch: for each of the four linears
+of a Llama-3-8B decoder layer (fused QKV 4096->6144, O 4096->4096, fused
+gate_up 4096->28672, down 14336->4096), dynamic per-tensor quantization of
+the bf16 activations, then the scaled FP8 GEMM with channelwise weight
+scales and the rescale fused into its bf16 store.
+
+Workloads (synthetic, seeded; the models' shapes only -- no checkpoints):
+  decode   M = 16 tokens.  HBM-bound: reported in GB/s of algorithmic bytes.
+           The weights rotate through 8 distinct copies of the layer
+           (1.75 GB, several times the 256 MB Infinity Cache), as successive
+           layers of a model would, so they stream from HBM.
+  prefill  M = 16 x 1024 = 16384 tokens.  Matrix-core bound: TFLOP/s.
+
+Prints ONE JSON line.  The roofline object describes the dominant kernel
+(the GEMM), timed per launch with HIP events on the launch stream; the
+cpu_baseline object times the CPU oracle on a bounded sample of the same
+workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import fp8_w8a8_quantized_amd as fp8  # noqa: E402
+from fp8_w8a8_quantized_amd import synth  # noqa: E402
+
+METRIC = "W8A8 scaled-GEMM TFLOP/s (% FP8 MFMA peak); decode M≤16 GB/s (% HBM peak)"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 matrix throughput, published
+ROTATE_DECODE = 8
+
+
+def quant_bytes(m, k):
+    """Algorithmic HBM bytes of dynamic quantization: read bf16, write codes + scale."""
+    return 2 * m * k + m * k + 4
+
+
+def gemm_bytes(m, k, n, per_channel=True):
+    """Algorithmic HBM bytes of the scaled GEMM: W and A codes once, bf16 out, scales."""
+    return n * k + m * k + 2 * m * n + (4 * n if per_channel else 4) + 4
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_layer(m, rotate):
+    """Quantized weights (on the GPU, per channel) and bf16 activations."""
+    lin = []
+    for sub, (name, k, n) in enumerate(synth.LLAMA3_8B_LINEARS):
+        w = synth.bf16_bits_to_torch(synth.weights(2, n, k, sub=sub, row_multipliers=True)).cuda()
+        w_q, s_w = fp8.quant_weight(w, per_channel=True)
+        del w
+        copies = [(w_q, s_w)] + [(w_q.clone(), s_w.clone()) for _ in range(rotate - 1)]
+        x = synth.bf16_bits_to_torch(synth.activations(2, m, k, sub=sub, outliers=True)).cuda()
+        lin.append(dict(name=name, k=k, n=n, x=x, copies=copies,
+                        a_q=torch.empty((m, k), dtype=torch.uint8, device="cuda"),
+                        s_a=torch.empty(1, dtype=torch.float32, device="cuda"),
+                        out=torch.empty((m, n), dtype=torch.bfloat16, device="cuda")))
+    torch.cuda.synchronize()
+    return lin
+
+
+def run_step(lin, it, ws, events=None):
+    for j, L in enumerate(lin):
+        w_q, s_w = L["copies"][it % len(L["copies"])]
+        fp8.quant_dynamic(L["x"], workspace=ws, q=L["a_q"], scale=L["s_a"])
+        if events is not None:
+            events[j][0].record()
+        fp8.scaled_mm(L["a_q"], w_q, L["s_a"], s_w, True, out=L["out"])
+        if events is not None:
+            events[j][1].record()
+
+
+def cpu_baseline(m, lin_shapes, row_frac=8, budget_s=10.0):
+    """Time the CPU oracle on a bounded sample of the same workload.
+
+    Sample: each of the four linears restricted to its first N / row_frac
+    output channels (same K, same M, same generators), quantized once
+    (load-time work, untimed); then oracle steps (dynamic activation
+    quantization + exact GEMM + epilogue for the four linears) repeat until
+    about budget_s of timed work.  Returns (bytes, flops, seconds, threads,
+    description) for the timed steps.
+    """
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    prepared = []
+    for sub, (name, k, n) in enumerate(lin_shapes):
+        ns = max(1, n // row_frac)
+        x = synth.activations(2, m, k, sub=sub, outliers=True)
+        # the first ns rows of the full seeded weight (the streams are row-major)
+        w = synth.weights(2, ns, k, sub=sub, row_multipliers=True)
+        wq, sw = oracle.quant_weight(w, per_channel=True)
+        prepared.append((name, k, ns, x, wq, sw))
+    done_bytes = done_flops = 0
+    timed = 0.0
+    steps = 0
+    while steps == 0 or timed < budget_s:
+        for (name, k, ns, x, wq, sw) in prepared:
+            t0 = time.perf_counter()
+            aq, sa = oracle.quant_dynamic(x)
+            oracle.scaled_mm(aq, wq, sa, sw, True)
+            timed += time.perf_counter() - t0
+            done_bytes += quant_bytes(m, k) + gemm_bytes(m, k, ns)
+            done_flops += 2 * m * k * ns
+        steps += 1
+    desc = (f"{steps} oracle steps over the 4 linears at M={m} with N/{row_frac} output channels each "
+            f"({timed:.1f} s timed; weight quantization untimed; element-wise NumPy on 1 thread, "
+            f"fp64 BLAS matmul on {threads})")
+    return done_bytes, done_flops, timed, threads, desc
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", choices=["decode", "prefill"], default="decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the layer would shard column-parallel over N; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+    decode = args.workload == "decode"
+    m = 16 if decode else 16384
+    steps = args.steps if args.steps is not None else (200 if decode else 20)
+    warmup = args.warmup if args.warmup is not None else (20 if decode else 3)
+    rotate = ROTATE_DECODE if decode else 1
+    torch.cuda.set_device(0)
+
+    log(f"building inputs: {args.workload}, M={m}, rotate={rotate}")
+    lin = build_layer(m, rotate)
+    ws = fp8.new_workspace()
+    for i in range(warmup):
+        run_step(lin, i, ws)
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for i in range(steps):
+        run_step(lin, i, ws)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+
+    # per-launch GEMM durations with HIP events on the launch stream
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in lin] for _ in range(steps)]
+    for i in range(steps):
+        run_step(lin, i, ws, events=[(a, b) for (a, b) in ev[i]])
+    torch.cuda.synchronize()
+    gemm_ms = np.array([[a.elapsed_time(b) for (a, b) in ev[i]] for i in range(steps)])  # [steps, 4]
+
+    step_bytes = sum(quant_bytes(m, L["k"]) + gemm_bytes(m, L["k"], L["n"]) for L in lin)
+    step_flops = sum(2 * m * L["k"] * L["n"] for L in lin)
+    per_launch_bytes = np.mean([gemm_bytes(m, L["k"], L["n"]) for L in lin])
+    per_launch_flops = np.mean([2 * m * L["k"] * L["n"] for L in lin])
+    avg_launch_s = gemm_ms.mean() * 1e-3
+    per_shape_us = {L["name"]: round(float(gemm_ms[:, j].mean() * 1e3), 2) for j, L in enumerate(lin)}
+
+    if decode:
+        value = step_bytes / (ms_per_step * 1e-3) / 1e9
+        unit = "GB/s"
+        achieved = per_launch_bytes / avg_launch_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "gemm_skinny_kernel<4, 8, true>", "avg_launch_us": round(avg_launch_s * 1e6, 2),
+                "per_shape_us": per_shape_us}
+    else:
+        value = step_flops / (ms_per_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        achieved = per_launch_flops / avg_launch_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "gemm_mfma_kernel", "avg_launch_us": round(avg_launch_s * 1e6, 2),
+                "per_shape_us": per_shape_us}
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3 (fp32 accumulate, bf16 out)",
+        "data": "synthetic",
+        "config": {"workload": f"llama3-8b {'decode' if decode else 'prefill'} linears (qkv, o, gate_up, down), "
+                               f"M={m}, channelwise weight scales, dynamic per-tensor activation scale"
+                               + (f", weights rotated over {rotate} layer copies" if rotate > 1 else ""),
+                   "M": m, "shapes_kn": [[L["k"], L["n"]] for L in lin]},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        del lin
+        torch.cuda.empty_cache()
+        shapes = synth.LLAMA3_8B_LINEARS
+        cm = m if decode else 64          # prefill sample: 64 of the 16384 rows
+        nbytes, nflops, secs, threads, desc = cpu_baseline(cm, shapes)
+        if decode:
+            cv, cu = nbytes / secs / 1e9, "GB/s"
+        else:
+            cv, cu = nflops / secs / 1e12, "TFLOP/s"
+        line["cpu_baseline"] = {
+            "value": round(cv, 4), "unit": cu, "cores": threads, "kind": "oracle",
+            "sample": desc}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

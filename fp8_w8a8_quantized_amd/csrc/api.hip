@@ -1,0 +1,130 @@
+// C ABI of the FP8 W8A8 linear layer: host-side validation and dispatch.
+// Every argument check runs before any HIP call, so invalid calls fail
+// without touching the device (and work on machines without a GPU).
+
+#include <stdio.h>
+#include <stdarg.h>
+
+#include "../../include/fp8w8a8.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fp8_status fail(fp8_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+fp8_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return FP8_OK;
+  return fail(FP8_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+}
+
+// Shared checks of the quantization calls.  Element counts are capped so
+// that units of 8 elements index in 32 bits.
+fp8_status check_quant(const char* fn, const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                       const uint8_t* q, int64_t ld_q) {
+  if (rows < 0 || cols < 0) return fail(FP8_ERR_INVALID_ARG, "%s: negative size (rows=%lld, cols=%lld)", fn,
+                                        (long long)rows, (long long)cols);
+  if (ld_x < cols || ld_q < cols)
+    return fail(FP8_ERR_INVALID_ARG, "%s: leading dimension smaller than cols (ld_x=%lld, ld_q=%lld, cols=%lld)",
+                fn, (long long)ld_x, (long long)ld_q, (long long)cols);
+  if (rows > 0 && cols > 0 && (x == nullptr || q == nullptr))
+    return fail(FP8_ERR_INVALID_ARG, "%s: null input or output pointer", fn);
+  if (rows > 0 && cols > 0 && (rows * ((cols + 7) / 8) >= (1ll << 32) || rows >= (1ll << 31)))
+    return fail(FP8_ERR_UNSUPPORTED, "%s: tensor too large (rows=%lld, cols=%lld)", fn, (long long)rows,
+                (long long)cols);
+  return FP8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fp8_quant_workspace_bytes(void) { return fp8w8a8::quant_workspace_bytes(); }
+
+const char* fp8_last_error(void) { return g_err; }
+
+fp8_status fp8_quant_dynamic(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q_e4m3,
+                             int64_t ld_q, float* scale_out, void* workspace, void* stream) {
+  const char* fn = "fp8_quant_dynamic";
+  fp8_status st = check_quant(fn, x_bf16, rows, cols, ld_x, q_e4m3, ld_q);
+  if (st != FP8_OK) return st;
+  if (scale_out == nullptr) return fail(FP8_ERR_INVALID_ARG, "%s: null scale_out", fn);
+  if (rows > 0 && cols > 0 && workspace == nullptr) return fail(FP8_ERR_INVALID_ARG, "%s: null workspace", fn);
+  return hip_status(fp8w8a8::launch_quant_dynamic(x_bf16, rows, cols, ld_x, q_e4m3, ld_q, scale_out, workspace,
+                                                  static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+fp8_status fp8_quant_static(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, const float* scale,
+                            uint8_t* q_e4m3, int64_t ld_q, void* stream) {
+  const char* fn = "fp8_quant_static";
+  fp8_status st = check_quant(fn, x_bf16, rows, cols, ld_x, q_e4m3, ld_q);
+  if (st != FP8_OK) return st;
+  if (scale == nullptr) return fail(FP8_ERR_INVALID_ARG, "%s: null scale", fn);
+  return hip_status(fp8w8a8::launch_quant_static(x_bf16, rows, cols, ld_x, scale, q_e4m3, ld_q,
+                                                 static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+fp8_status fp8_quant_dynamic_per_row(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                                     uint8_t* q_e4m3, int64_t ld_q, float* scales_out, void* stream) {
+  const char* fn = "fp8_quant_dynamic_per_row";
+  fp8_status st = check_quant(fn, x_bf16, rows, cols, ld_x, q_e4m3, ld_q);
+  if (st != FP8_OK) return st;
+  if (rows > 0 && scales_out == nullptr) return fail(FP8_ERR_INVALID_ARG, "%s: null scales_out", fn);
+  return hip_status(fp8w8a8::launch_quant_per_row(x_bf16, rows, cols, ld_x, q_e4m3, ld_q, scales_out,
+                                                  static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+fp8_status fp8_scaled_mm(const uint8_t* a_q, int64_t lda, const uint8_t* w_q, int64_t ldw, const float* s_a,
+                         const float* s_w, fp8_scale_mode mode, fp8_accum_mode accum, const uint16_t* bias_bf16,
+                         uint16_t* out_bf16, int64_t ldo, int64_t M, int64_t N, int64_t K, void* stream) {
+  const char* fn = "fp8_scaled_mm";
+  if (M < 0 || N < 0) return fail(FP8_ERR_INVALID_ARG, "%s: negative M or N (M=%lld, N=%lld)", fn,
+                                  (long long)M, (long long)N);
+  if (K < 1) return fail(FP8_ERR_INVALID_ARG, "%s: K must be >= 1 (K=%lld)", fn, (long long)K);
+  if (lda < K || ldw < K) return fail(FP8_ERR_INVALID_ARG, "%s: lda/ldw smaller than K", fn);
+  if (ldo < N) return fail(FP8_ERR_INVALID_ARG, "%s: ldo smaller than N", fn);
+  if (mode != FP8_SCALE_PER_TENSOR && mode != FP8_SCALE_PER_CHANNEL)
+    return fail(FP8_ERR_INVALID_ARG, "%s: unknown scale mode %d", fn, (int)mode);
+  if (accum != FP8_ACCUM_FP32 && accum != FP8_ACCUM_FP8_MFMA)
+    return fail(FP8_ERR_INVALID_ARG, "%s: unknown accumulation mode %d", fn, (int)accum);
+  if (a_q == nullptr || w_q == nullptr || s_a == nullptr || s_w == nullptr || out_bf16 == nullptr)
+    return fail(FP8_ERR_INVALID_ARG, "%s: null required pointer", fn);
+  if (M >= (1ll << 31) || N >= (1ll << 31) || K >= (1ll << 30) || lda >= (1ll << 40) || ldw >= (1ll << 40))
+    return fail(FP8_ERR_UNSUPPORTED, "%s: problem too large", fn);
+  if (M == 0 || N == 0) return FP8_OK;
+
+  fp8w8a8::GemmArgs g;
+  g.a = a_q; g.w = w_q; g.s_a = s_a; g.s_w = s_w; g.bias = bias_bf16; g.out = out_bf16;
+  g.lda = lda; g.ldw = ldw; g.ldo = ldo;
+  g.M = (int32_t)M; g.N = (int32_t)N; g.K = (int32_t)K;
+  g.per_channel = mode == FP8_SCALE_PER_CHANNEL ? 1 : 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (M > 64 && tiles < (1ll << 31) && fp8w8a8::gemm_mfma_supported(g))
+    return hip_status(fp8w8a8::launch_gemm_mfma(g, accum == FP8_ACCUM_FP8_MFMA, s), fn);
+
+  // Skinny kernel, in slices of at most 65535 blocks of 16 rows (grid.y).
+  const int64_t slice = 65535ll * 16;
+  for (int64_t m0 = 0; m0 < M; m0 += slice) {
+    fp8w8a8::GemmArgs gs = g;
+    gs.a = a_q + m0 * lda;
+    gs.out = out_bf16 + m0 * ldo;
+    gs.M = (int32_t)((M - m0) < slice ? (M - m0) : slice);
+    fp8_status st = hip_status(fp8w8a8::launch_gemm_skinny(gs, s), fn);
+    if (st != FP8_OK) return st;
+  }
+  return FP8_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,120 @@
+// Device helpers shared by the gfx950 kernels of the FP8 W8A8 linear layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8w8a8 {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kE4M3Max = 448.0f;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// float32 -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Per-tensor scale from amax: amax / 448 correctly rounded in float32; an
+// all-zero tensor has no range to map and takes scale 1.
+__device__ __forceinline__ float scale_from_amax(float amax) {
+  return amax == 0.0f ? 1.0f : amax / kE4M3Max;
+}
+
+// Saturating round-to-nearest-even e4m3fn codes for four values divided by s.
+// The division is the correctly rounded float32 one (the compiler's default
+// for '/'), then the quotient is clamped to +-448 and converted by the
+// hardware's fp8 conversion, which rounds to nearest even (OCP E4M3 codes on
+// gfx950) but turns magnitudes past 464 into NaN -- hence the clamp.
+__device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, float s) {
+  float qa = __builtin_amdgcn_fmed3f(a / s, -kE4M3Max, kE4M3Max);
+  float qb = __builtin_amdgcn_fmed3f(b / s, -kE4M3Max, kE4M3Max);
+  float qc = __builtin_amdgcn_fmed3f(c / s, -kE4M3Max, kE4M3Max);
+  float qd = __builtin_amdgcn_fmed3f(d / s, -kE4M3Max, kE4M3Max);
+  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(qa, qb, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(qc, qd, w, true);
+}
+
+__device__ __forceinline__ uint32_t quant1(float a, float s) {
+  float q = __builtin_amdgcn_fmed3f(a / s, -kE4M3Max, kE4M3Max);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(q, 0.0f, 0, false) & 0xffu;
+}
+
+// Quantize 8 bf16 values packed in a 16-byte word into 8 e4m3fn bytes.
+__device__ __forceinline__ uint2 quant8(v4i x, float s) {
+  uint2 r;
+  r.x = quant4(bf16_to_f32(x[0] & 0xffff), bf16_to_f32((uint32_t)x[0] >> 16),
+               bf16_to_f32(x[1] & 0xffff), bf16_to_f32((uint32_t)x[1] >> 16), s);
+  r.y = quant4(bf16_to_f32(x[2] & 0xffff), bf16_to_f32((uint32_t)x[2] >> 16),
+               bf16_to_f32(x[3] & 0xffff), bf16_to_f32((uint32_t)x[3] >> 16), s);
+  return r;
+}
+
+// Largest |bf16| among 8 packed values, as the 15-bit magnitude pattern.
+// For finite bf16 the magnitude bits order like the magnitudes themselves.
+__device__ __forceinline__ uint32_t absmax_bits8(v4i x) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t w = (uint32_t)x[i];
+    m = max(m, w & 0x7fffu);
+    m = max(m, (w >> 16) & 0x7fffu);
+  }
+  return m;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return v;
+}
+
+// Block-wide max; every thread gets the result.  `red` holds >= 16 words.
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
+  v = wave_max_u32(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nwaves = (blockDim.x + 63) >> 6;
+  __syncthreads();  // red may be in use by a previous call
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  uint32_t r = 0;
+  for (int w = 0; w < nwaves; ++w) r = max(r, red[w]);
+  return r;
+}
+
+// Exact unsigned 32-bit division by a run-time invariant divisor with one
+// multiply-high, after Granlund and Montgomery, "Division by invariant
+// integers using multiplication" (PLDI 1994), figure 4.1.
+struct FastDivU32 {
+  uint32_t d, m, s1, s2;
+};
+
+__host__ __device__ inline FastDivU32 make_fastdiv(uint32_t d) {
+  FastDivU32 f;
+  f.d = d;
+  uint32_t l = 0;
+  while (l < 32 && (1ull << l) < d) ++l;
+  f.m = (uint32_t)((((1ull << l) - d) << 32) / d + 1);
+  f.s1 = l < 1 ? l : 1;
+  f.s2 = l > 0 ? l - 1 : 0;
+  return f;
+}
+
+__device__ __forceinline__ uint32_t fastdiv(uint32_t n, const FastDivU32& f) {
+  uint32_t t = __umulhi(f.m, n);
+  return (t + ((n - t) >> f.s1)) >> f.s2;
+}
+
+}  // namespace fp8w8a8

@@ -1,0 +1,40 @@
+// Launchers shared between the C-ABI layer and the kernel translation units.
+// Arguments reach these already validated (see api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp8w8a8 {
+
+size_t quant_workspace_bytes();
+
+hipError_t launch_quant_dynamic(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
+                                int64_t ld_q, float* scale_out, void* workspace, hipStream_t stream);
+hipError_t launch_quant_static(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, const float* scale,
+                               uint8_t* q, int64_t ld_q, hipStream_t stream);
+hipError_t launch_quant_per_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
+                                int64_t ld_q, float* scales_out, hipStream_t stream);
+
+struct GemmArgs {
+  const uint8_t* a;   // [M, K] e4m3fn, pitch lda
+  const uint8_t* w;   // [N, K] e4m3fn, pitch ldw
+  const float* s_a;   // 1 float
+  const float* s_w;   // 1 or N floats
+  const uint16_t* bias;  // N bf16 or null
+  uint16_t* out;      // [M, N] bf16, pitch ldo
+  int64_t lda, ldw, ldo;
+  int32_t M, N, K;
+  int32_t per_channel;
+};
+
+// Skinny path: any layout; one 16-row block of M per grid row.
+hipError_t launch_gemm_skinny(const GemmArgs& g, hipStream_t stream);
+// Matrix-core GEMM: requires 16-byte aligned a/w rows and K % 16 == 0.
+bool gemm_mfma_supported(const GemmArgs& g);
+// fp8_accumulate: fp8 matrix-core sums (fast, 13-bit group sums) instead of
+// the exact bf16 path.
+hipError_t launch_gemm_mfma(const GemmArgs& g, bool fp8_accumulate, hipStream_t stream);
+
+}  // namespace fp8w8a8

@@ -88,12 +88,13 @@ def quant_weight(w_bits, per_channel):
     if not per_channel:
         q, s = quant_dynamic(w_bits)
         return q, np.array([s], dtype=np.float32)
-    n = w_bits.shape[0]
-    q = np.empty(w_bits.shape, dtype=np.uint8)
-    s = np.empty(n, dtype=np.float32)
-    for i in range(n):
-        q[i], s[i] = quant_dynamic(w_bits[i])
-    return q, s
+    w = bf16_bits_to_f32(w_bits)
+    a = (np.max(np.abs(w), axis=1) if w.shape[1] else np.zeros(w.shape[0])).astype(np.float32)
+    # the per-tensor rule applied to each row: fl32(amax_n / 448), 1 when 0
+    s = np.where(a == 0, np.float32(1.0), a / _F32_MAX).astype(np.float32)
+    with np.errstate(over="ignore", divide="ignore", invalid="ignore"):
+        v = (w / s[:, None]).astype(np.float32)
+    return encode(v), s
 
 
 def gemm_exact(a_q, w_q):

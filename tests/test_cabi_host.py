@@ -1,0 +1,100 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/fp8w8a8.h declares, and rejects invalid arguments on the host before
+anything reaches the device (these calls make no HIP call at all)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_w8a8_quantized_amd as fp8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8w8a8.h")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+NULL = ctypes.c_void_p(0)
+P = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fp8.LIB_PATH):
+        pytest.skip("library not built")
+    return fp8.lib()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted([
+        "fp8_quant_workspace_bytes", "fp8_quant_dynamic", "fp8_quant_static",
+        "fp8_quant_dynamic_per_row", "fp8_scaled_mm", "fp8_last_error"])
+
+
+def test_library_exports_every_declared_function(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(fp8.SIGNATURES) == set(declared_functions())
+
+
+def test_workspace_size_is_small(lib):
+    n = lib.fp8_quant_workspace_bytes()
+    assert 0 < n <= 64 * 1024
+
+
+def _err(lib):
+    return lib.fp8_last_error().decode()
+
+
+def test_quant_dynamic_rejects_bad_arguments(lib):
+    f = lib.fp8_quant_dynamic
+    assert f(P, -1, 4, 4, P, 4, P, P, NULL) == INVALID
+    assert "negative" in _err(lib)
+    assert f(P, 2, 4, 3, P, 4, P, P, NULL) == INVALID        # ld_x < cols
+    assert f(P, 2, 4, 4, P, 3, P, P, NULL) == INVALID        # ld_q < cols
+    assert f(NULL, 2, 4, 4, P, 4, P, P, NULL) == INVALID     # null x
+    assert f(P, 2, 4, 4, NULL, 4, P, P, NULL) == INVALID     # null q
+    assert f(P, 2, 4, 4, P, 4, NULL, P, NULL) == INVALID     # null scale
+    assert f(P, 2, 4, 4, P, 4, P, NULL, NULL) == INVALID     # null workspace
+    assert f(P, 2 ** 33, 2 ** 10, 2 ** 10, P, 2 ** 10, P, P, NULL) == UNSUPPORTED
+
+
+def test_quant_static_and_per_row_reject_bad_arguments(lib):
+    assert lib.fp8_quant_static(P, 2, 4, 4, NULL, P, 4, NULL) == INVALID
+    assert lib.fp8_quant_static(P, 2, -4, 4, P, P, 4, NULL) == INVALID
+    assert lib.fp8_quant_dynamic_per_row(P, 2, 4, 4, P, 4, NULL, NULL) == INVALID
+    assert lib.fp8_quant_dynamic_per_row(P, 2, 8, 4, P, 8, P, NULL) == INVALID
+
+
+def test_scaled_mm_rejects_bad_arguments(lib):
+    f = lib.fp8_scaled_mm
+    good = dict(a=P, lda=64, w=P, ldw=64, sa=P, sw=P, mode=0, accum=0, bias=NULL, out=P, ldo=32, M=4, N=32, K=64)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return f(a["a"], a["lda"], a["w"], a["ldw"], a["sa"], a["sw"], a["mode"], a["accum"], a["bias"], a["out"],
+                 a["ldo"], a["M"], a["N"], a["K"], NULL)
+    assert call(M=-1) == INVALID
+    assert call(N=-2) == INVALID
+    assert call(K=0) == INVALID
+    assert call(lda=63) == INVALID
+    assert call(ldw=10) == INVALID
+    assert call(ldo=31) == INVALID
+    assert call(mode=2) == INVALID and "mode" in _err(lib)
+    assert call(accum=5) == INVALID and "accumulation" in _err(lib)
+    for p in ("a", "w", "sa", "sw", "out"):
+        assert call(**{p: NULL}) == INVALID, p
+    # empty problems are valid no-ops that launch nothing
+    assert call(M=0) == OK
+    assert call(N=0, ldo=0) == OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(fp8, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(fp8, "_lib", None)
+    with pytest.raises(fp8.Fp8Error, match="no fallback"):
+        fp8.lib()

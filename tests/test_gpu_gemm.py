@@ -1,0 +1,175 @@
+"""Scaled GEMM on the GPU vs the exact CPU oracle (element-wise tolerance)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp8_w8a8_quantized_amd as fp8
+from fp8_w8a8_quantized_amd import synth
+from _helpers import say, dev_bf16, host_u8, host_f32, host_bf16_bits, assert_gemm_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _prepare(cfg, m, k, n, per_channel, outliers=False, rowmul=False, with_bias=False, sub=0):
+    """Inputs from the seeded generators, quantized independently on each side;
+    the GPU's quantized operands must equal the oracle's byte for byte."""
+    x = synth.activations(cfg, m, k, sub=sub, outliers=outliers)
+    w = synth.weights(cfg, n, k, sub=sub, row_multipliers=rowmul)
+    b = synth.bias(cfg, n, sub=sub) if with_bias else None
+    a_q, s_a = fp8.quant_dynamic(dev_bf16(x))
+    w_q, s_w = fp8.quant_weight(dev_bf16(w), per_channel)
+    aq_ref, sa_ref = oracle.quant_dynamic(x)
+    wq_ref, sw_ref = oracle.quant_weight(w, per_channel)
+    torch.cuda.synchronize()
+    assert host_f32(s_a)[0] == sa_ref and np.array_equal(host_u8(a_q), aq_ref)
+    assert np.array_equal(host_f32(s_w), sw_ref) and np.array_equal(host_u8(w_q), wq_ref)
+    bias_d = dev_bf16(b) if b is not None else None
+    return dict(a_q=a_q, s_a=s_a, w_q=w_q, s_w=s_w, bias=bias_d, bias_bits=b,
+                aq=aq_ref, sa=sa_ref, wq=wq_ref, sw=sw_ref)
+
+
+def _run_and_check(d, per_channel, rows=None, accum="fp32"):
+    out = fp8.scaled_mm(d["a_q"], d["w_q"], d["s_a"], d["s_w"], per_channel, d["bias"], accum=accum)
+    torch.cuda.synchronize()
+    ob = host_bf16_bits(out)
+    aq = d["aq"] if rows is None else d["aq"][rows]
+    ref = oracle.scaled_mm(aq, d["wq"], d["sa"], d["sw"], per_channel, d["bias_bits"])
+    return assert_gemm_close(ob, ref, d["aq"], d["sa"], d["wq"], d["sw"], per_channel, rows=rows,
+                             bias_bits=d["bias_bits"], accum=accum), out
+
+
+# ------------------------------------------------------------- skinny (M <= 16)
+@pytest.mark.parametrize("m", [1, 3, 7, 13, 16])
+@pytest.mark.parametrize("k,n", [(4096, 4100), (4096, 1030), (4096, 4096)])
+def test_skinny_per_tensor_unaligned(m, k, n):
+    say("skinny per-tensor", m, k, n)
+    d = _prepare(4, m, k, n, per_channel=False)
+    _run_and_check(d, False)
+
+
+@pytest.mark.parametrize("m,k,n", [(16, 4096, 6144), (16, 14336, 4096), (5, 4096, 28672)])
+def test_skinny_per_channel_llama_shapes(m, k, n):
+    say("skinny per-channel", m, k, n)
+    d = _prepare(2, m, k, n, per_channel=True, outliers=True, rowmul=True, with_bias=(m == 5))
+    _run_and_check(d, True)
+
+
+@pytest.mark.parametrize("m,k,n", [(1, 1, 1), (2, 7, 3), (16, 100, 17), (9, 272, 33), (16, 16, 16), (4, 4099, 40)])
+def test_skinny_tiny_and_ragged_k(m, k, n):
+    say("skinny ragged", m, k, n)
+    d = _prepare(4, m, k, n, per_channel=True, with_bias=True, rowmul=True)
+    _run_and_check(d, True)
+
+
+# -------------------------------------------------- mid M (skinny over M blocks)
+@pytest.mark.parametrize("m,k,n", [(17, 4096, 1030), (33, 512, 4100), (64, 1024, 300)])
+def test_mid_m(m, k, n):
+    say("mid m", m, k, n)
+    d = _prepare(4, m, k, n, per_channel=False, with_bias=True)
+    _run_and_check(d, False)
+
+
+# ------------------------------------------------------ matrix-core GEMM (M > 64)
+@pytest.mark.parametrize("accum", ["fp32", "fp8"])
+@pytest.mark.parametrize("m,k,n,pc", [
+    (256, 256, 256, False), (512, 4096, 1024, True), (300, 4096, 4100, False),
+    (777, 1040, 520, True), (65, 128, 16, False), (1000, 4096, 6144, True)])
+def test_mfma_gemm(m, k, n, pc, accum):
+    say("mfma", m, k, n, pc, accum)
+    d = _prepare(3, m, k, n, per_channel=pc, outliers=pc, rowmul=pc, with_bias=(m % 2 == 0))
+    _run_and_check(d, pc, accum=accum)
+
+
+@pytest.mark.parametrize("accum", ["fp32", "fp8"])
+def test_mfma_gemm_k_not_multiple_of_128(accum):
+    d = _prepare(3, 320, 4096 + 48, 512, per_channel=True, rowmul=True)
+    _run_and_check(d, True, accum=accum)
+
+
+@pytest.mark.parametrize("m", [16, 300])
+@pytest.mark.parametrize("accum", ["fp32", "fp8"])
+def test_every_code_through_identity_weight(m, accum):
+    """W_q = 0x38 * I (weight 1.0) makes each output one product:
+    out[m, n] = dec(A_q[m, n]) * s_a * s_w exactly, for all 254 finite codes."""
+    k = 256
+    codes = np.arange(256, dtype=np.uint8)
+    codes[[0x7F, 0xFF]] = 0
+    rng = np.random.default_rng(m)
+    a = np.stack([rng.permutation(codes) for _ in range(m)])
+    w = np.where(np.eye(k, dtype=bool), np.uint8(0x38), np.uint8(0))
+    s_a = torch.tensor([0.25], dtype=torch.float32, device="cuda")
+    s_w = torch.tensor([2.0], dtype=torch.float32, device="cuda")
+    out = fp8.scaled_mm(torch.from_numpy(a).cuda(), torch.from_numpy(w).cuda(), s_a, s_w, False, accum=accum)
+    torch.cuda.synchronize()
+    want = oracle.decode(a) * 0.5
+    got = oracle.bf16_bits_to_f32(host_bf16_bits(out)).astype(np.float64)
+    assert np.array_equal(got, want)
+
+
+def test_unaligned_layout_falls_back_correctly():
+    """Row pitches that are not multiples of 16 bytes (M > 64): generic path."""
+    m, k, n = 130, 1000, 200
+    x = synth.activations(8, m, k); w = synth.weights(8, n, k)
+    xa = torch.zeros((m, 1003), dtype=torch.bfloat16, device="cuda"); xa[:, :k] = dev_bf16(x)
+    wa = torch.zeros((n, 1001), dtype=torch.bfloat16, device="cuda"); wa[:, :k] = dev_bf16(w)
+    a_q, s_a = fp8.quant_dynamic(xa[:, :k], q=torch.empty((m, 1001), dtype=torch.uint8, device="cuda")[:, :k])
+    w_q, s_w = fp8.quant_dynamic(wa[:, :k], q=torch.empty((n, 1005), dtype=torch.uint8, device="cuda")[:, 1:k + 1])
+    outbuf = torch.full((m, n + 7), -7.0, dtype=torch.bfloat16, device="cuda")
+    out = fp8.scaled_mm(a_q, w_q, s_a, s_w, False, out=outbuf[:, 3:n + 3])
+    torch.cuda.synchronize()
+    aq, sa = oracle.quant_dynamic(x); wq, sw = oracle.quant_weight(w, False)
+    ref = oracle.scaled_mm(aq, wq, sa, sw, False)
+    assert_gemm_close(host_bf16_bits(out), ref, aq, sa, wq, sw, False)
+    ob = outbuf.float().cpu().numpy()
+    assert np.all(ob[:, :3] == -7.0) and np.all(ob[:, n + 3:] == -7.0)
+
+
+# -------------------------------------------------------------- invariants
+@pytest.mark.parametrize("m,n", [(16, 4096), (512, 1024)])
+def test_per_channel_equal_scales_bit_exact_with_per_tensor(m, n):
+    k = 4096
+    d = _prepare(1, m, k, n, per_channel=False)
+    sig = d["s_w"]
+    s_vec = sig.repeat(n).contiguous()
+    o1 = fp8.scaled_mm(d["a_q"], d["w_q"], d["s_a"], sig, False)
+    o2 = fp8.scaled_mm(d["a_q"], d["w_q"], d["s_a"], s_vec, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_output_canaries_and_pitch():
+    m, k, n = 300, 512, 1030
+    d = _prepare(5, m, k, n, per_channel=True, rowmul=True)
+    buf = torch.full((m + 2, n + 9), 3.0, dtype=torch.bfloat16, device="cuda")
+    out = buf[1:m + 1, 4:n + 4]
+    fp8.scaled_mm(d["a_q"], d["w_q"], d["s_a"], d["s_w"], True, out=out)
+    torch.cuda.synchronize()
+    h = buf.float().cpu().numpy()
+    assert np.all(h[0] == 3.0) and np.all(h[-1] == 3.0)
+    assert np.all(h[:, :4] == 3.0) and np.all(h[:, n + 4:] == 3.0)
+    ref = oracle.scaled_mm(d["aq"], d["wq"], d["sa"], d["sw"], True)
+    assert_gemm_close(host_bf16_bits(out), ref, d["aq"], d["sa"], d["wq"], d["sw"], True)
+
+
+def test_gemm_deterministic():
+    d = _prepare(6, 1024, 4096, 2048, per_channel=True, rowmul=True)
+    o1 = fp8.scaled_mm(d["a_q"], d["w_q"], d["s_a"], d["s_w"], True)
+    o2 = fp8.scaled_mm(d["a_q"], d["w_q"], d["s_a"], d["s_w"], True)
+    d2 = _prepare(6, 16, 4096, 2048, per_channel=True, rowmul=True)
+    o3 = fp8.scaled_mm(d2["a_q"], d2["w_q"], d2["s_a"], d2["s_w"], True)
+    o4 = fp8.scaled_mm(d2["a_q"], d2["w_q"], d2["s_a"], d2["s_w"], True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(o3.view(torch.int16), o4.view(torch.int16))
+
+
+def test_zero_activations_give_bias():
+    n, k = 1030, 4096
+    w = synth.weights(1, n, k); b = synth.bias(1, n)
+    w_q, s_w = fp8.quant_weight(dev_bf16(w), True)
+    for m in (16, 200):
+        a_q, s_a = fp8.quant_dynamic(torch.zeros((m, k), dtype=torch.bfloat16, device="cuda"))
+        out = fp8.scaled_mm(a_q, w_q, s_a, s_w, True, dev_bf16(b))
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bf16_bits(out), np.broadcast_to(b, (m, n)))
