@@ -13,10 +13,14 @@ Workloads (synthetic, seeded; the models' shapes only -- no checkpoints):
            layers of a model would, so they stream from HBM.
   prefill  M = 16 x 1024 = 16384 tokens.  Matrix-core bound: TFLOP/s.
 
+Each step is captured once into a HIP graph and replayed (as a serving
+loop would); --eager launches every kernel from Python instead.
+
 Prints ONE JSON line.  The roofline object describes the dominant kernel
-(the GEMM), timed per launch with HIP events on the launch stream; the
-cpu_baseline object times the CPU oracle on a bounded sample of the same
-workload.
+(the GEMM): algorithmic bytes (decode) or flops (prefill) per launch over
+the mean launch time, measured with HIP events around graphs of
+back-to-back GEMM launches; the cpu_baseline object times the CPU oracle on
+a bounded sample of the same workload.
 """
 import argparse
 import json
@@ -70,15 +74,11 @@ def build_layer(m, rotate):
     return lin
 
 
-def run_step(lin, it, ws, events=None):
-    for j, L in enumerate(lin):
+def run_step(lin, it, ws, accum):
+    for L in lin:
         w_q, s_w = L["copies"][it % len(L["copies"])]
         fp8.quant_dynamic(L["x"], workspace=ws, q=L["a_q"], scale=L["s_a"])
-        if events is not None:
-            events[j][0].record()
-        fp8.scaled_mm(L["a_q"], w_q, L["s_a"], s_w, True, out=L["out"])
-        if events is not None:
-            events[j][1].record()
+        fp8.scaled_mm(L["a_q"], w_q, L["s_a"], s_w, True, out=L["out"], accum=accum)
 
 
 def cpu_baseline(m, lin_shapes, row_frac=8, budget_s=10.0):
@@ -129,7 +129,14 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", choices=["decode", "prefill"], default="decode")
+    ap.add_argument("--accum", choices=["fp32", "fp8"], default="fp32",
+                    help="GEMM accumulation: fp32-class sums (default) or the fp8 matrix cores (M > 16)")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every kernel from Python instead of replaying captured HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run a fill, a device copy (3 times) and a sum over a buffer of this "
+                         "many MiB, so that profiler byte counters can be scaled against kernels of known traffic")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -146,29 +153,73 @@ def main():
     lin = build_layer(m, rotate)
     ws = fp8.new_workspace()
     for i in range(warmup):
-        run_step(lin, i, ws)
+        run_step(lin, i, ws, args.accum)
     torch.cuda.synchronize()
+
+    if args.eager:
+        def step_fn(i):
+            run_step(lin, i, ws, args.accum)
+    else:
+        # one HIP graph per weight copy; the library calls allocate nothing and
+        # never synchronize, so a whole step (8 launches) replays as one graph
+        step_graphs = []
+        for r in range(rotate):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run_step(lin, r, ws, args.accum)
+            step_graphs.append(g)
+        torch.cuda.synchronize()
+
+        def step_fn(i):
+            step_graphs[i % rotate].replay()
+        for i in range(warmup):
+            step_fn(i)
+        torch.cuda.synchronize()
 
     t0 = time.perf_counter()
     for i in range(steps):
-        run_step(lin, i, ws)
+        step_fn(i)
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
 
-    # per-launch GEMM durations with HIP events on the launch stream
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in lin] for _ in range(steps)]
-    for i in range(steps):
-        run_step(lin, i, ws, events=[(a, b) for (a, b) in ev[i]])
-    torch.cuda.synchronize()
-    gemm_ms = np.array([[a.elapsed_time(b) for (a, b) in ev[i]] for i in range(steps)])  # [steps, 4]
+    # Per-launch GEMM time: for each linear, a graph of back-to-back GEMM
+    # launches over the weight copies, bracketed by HIP events on the stream
+    # the launches run on; mean time per launch.
+    reps = max(1, 16 // rotate) if decode else 3
+    per_shape_s = []
+    for L in lin:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for rep in range(reps):
+                for r in range(rotate):
+                    w_q, s_w = L["copies"][r]
+                    fp8.scaled_mm(L["a_q"], w_q, L["s_a"], s_w, True, out=L["out"], accum=args.accum)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per_shape_s.append(e0.elapsed_time(e1) * 1e-3 / (3 * reps * rotate))
+
+    if args.copy_calibration_mib > 0:
+        nb = args.copy_calibration_mib << 20
+        src = torch.ones(nb, dtype=torch.uint8, device="cuda")   # fill: writes nb bytes
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)                                         # copy: reads and writes nb
+        total = src.view(torch.int32).sum()                        # reduction: reads nb
+        torch.cuda.synchronize()
+        del src, dst, total
 
     step_bytes = sum(quant_bytes(m, L["k"]) + gemm_bytes(m, L["k"], L["n"]) for L in lin)
     step_flops = sum(2 * m * L["k"] * L["n"] for L in lin)
     per_launch_bytes = np.mean([gemm_bytes(m, L["k"], L["n"]) for L in lin])
     per_launch_flops = np.mean([2 * m * L["k"] * L["n"] for L in lin])
-    avg_launch_s = gemm_ms.mean() * 1e-3
-    per_shape_us = {L["name"]: round(float(gemm_ms[:, j].mean() * 1e3), 2) for j, L in enumerate(lin)}
+    avg_launch_s = float(np.mean(per_shape_s))
+    per_shape_us = {L["name"]: round(per_shape_s[j] * 1e6, 2) for j, L in enumerate(lin)}
 
     if decode:
         value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -176,7 +227,7 @@ def main():
         achieved = per_launch_bytes / avg_launch_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "gemm_skinny_kernel<4, 8, true>", "avg_launch_us": round(avg_launch_s * 1e6, 2),
+                "kernel": "gemm_skinny_kernel<2>", "avg_launch_us": round(avg_launch_s * 1e6, 2),
                 "per_shape_us": per_shape_us}
     else:
         value = step_flops / (ms_per_step * 1e-3) / 1e12
@@ -184,18 +235,20 @@ def main():
         achieved = per_launch_flops / avg_launch_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None,
-                "kernel": "gemm_mfma_kernel", "avg_launch_us": round(avg_launch_s * 1e6, 2),
+                "kernel": f"gemm_mfma_kernel<{'false' if args.accum == 'fp8' else 'true'}>", "avg_launch_us": round(avg_launch_s * 1e6, 2),
                 "per_shape_us": per_shape_us}
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": steps,
         "warmup": warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3 (fp32 accumulate, bf16 out)",
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3 in, bf16 out; " + ("fp8 matrix-core sums" if args.accum == "fp8" and not decode
+                                              else "fp32-class sums (bf16 matrix cores on exact e4m3 values)"),
         "data": "synthetic",
         "config": {"workload": f"llama3-8b {'decode' if decode else 'prefill'} linears (qkv, o, gate_up, down), "
                                f"M={m}, channelwise weight scales, dynamic per-tensor activation scale"
                                + (f", weights rotated over {rotate} layer copies" if rotate > 1 else ""),
-                   "M": m, "shapes_kn": [[L["k"], L["n"]] for L in lin]},
+                   "M": m, "shapes_kn": [[L["k"], L["n"]] for L in lin],
+                   "launch": "eager" if args.eager else "hip_graph"},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -36,7 +36,7 @@ fp8_status check_quant(const char* fn, const uint16_t* x, int64_t rows, int64_t 
                 fn, (long long)ld_x, (long long)ld_q, (long long)cols);
   if (rows > 0 && cols > 0 && (x == nullptr || q == nullptr))
     return fail(FP8_ERR_INVALID_ARG, "%s: null input or output pointer", fn);
-  if (rows > 0 && cols > 0 && (rows * ((cols + 7) / 8) >= (1ll << 32) || rows >= (1ll << 31)))
+  if (rows > 0 && cols > 0 && rows * ((cols + 7) / 8) >= (1ll << 31))
     return fail(FP8_ERR_UNSUPPORTED, "%s: tensor too large (rows=%lld, cols=%lld)", fn, (long long)rows,
                 (long long)cols);
   return FP8_OK;

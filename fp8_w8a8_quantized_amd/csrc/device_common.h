@@ -15,6 +15,11 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kE4M3Max = 448.0f;
 
+// s_waitcnt immediate for gfx9: lgkmcnt(0), vmcnt and expcnt left at max.
+constexpr int kWaitLgkm0 = 0xC07F;
+// s_waitcnt immediate for gfx9: vmcnt(0), expcnt and lgkmcnt left at max.
+constexpr int kWaitVm0 = 0x0F70;
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }

@@ -14,11 +14,13 @@
 //   * Both operands are K-contiguous ([M, K] and [N, K]), which is the
 //     matrix cores' native operand layout: every lane reads 32 contiguous
 //     k-bytes of one row, so no transposition is needed anywhere.
-//   * Global -> registers -> LDS, double-buffered (2 x 64 KiB); the next
-//     step's loads are in flight while the current step's 32 MFMAs run.
-//     Loads are buffer loads whose out-of-range lanes (rows past M or N, k
-//     past K) return zeros, so edge tiles need no branches and k tails add
-//     nothing.
+//   * Global -> LDS directly (buffer_load ... lds, no staging registers),
+//     double-buffered (2 x 64 KiB); the next step's loads are in flight
+//     while the current step's products run.  Out-of-range lanes (rows past
+//     M or N, k past K) return zeros, so edge tiles need no branches and k
+//     tails add nothing.  Each k step reads all its fragments first and
+//     interleaves the remaining LDS reads and the next step's loads with
+//     the matrix products (scheduling barriers).
 //   * LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at
 //     position c ^ (r & 7), so the 8 rows that 8 consecutive lanes read land
 //     in 8 different bank groups.
@@ -106,37 +108,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)abase, (short)0, (int)nrec_a, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)wbase, (short)0, (int)nrec_w, kRsrcWord3);
 
-  // ---- loader: per stage each thread moves 8 chunks of 16 B per operand;
-  // chunk id = i * 256 + tid -> row = i * 32 + tid / 8, chunk = tid % 8.
-  const int lc = tid & 7;
-  const int lrow0 = tid >> 3;
-  uint32_t voff_a[8], voff_w[8];
+  // ---- loader: buffer_load_dwordx4 ... lds.  Each wave instruction fills
+  // one dense 1 KiB LDS block (8 rows x 128 bytes, lane i -> bytes 16i ..
+  // 16i+15, the block's base in M0); the XOR swizzle is applied by choosing
+  // which global chunk each lane fetches.  Block b of an operand is loaded
+  // by wave b / 8.  Out-of-range lanes (rows past M or N, k past K, or a
+  // whole step past the end) return zeros.
+  uint32_t dvoff_a[8], dvoff_w[8];
+  const int drow_in_blk = lane >> 3, dphys = lane & 7;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int row = i * 32 + lrow0;
-    voff_a[i] = row < rows_a ? (uint32_t)(row * g.lda + lc * 16) : kOutOfRange;
-    voff_w[i] = row < rows_w ? (uint32_t)(row * g.ldw + lc * 16) : kOutOfRange;
+    const int row = (wave * 8 + i) * 8 + drow_in_blk;
+    const int c = dphys ^ (row & 7);
+    dvoff_a[i] = row < rows_a ? (uint32_t)(row * g.lda + c * 16) : kOutOfRange;
+    dvoff_w[i] = row < rows_w ? (uint32_t)(row * g.ldw + c * 16) : kOutOfRange;
   }
-
-  v4i sa_regs[8], sw_regs[8];
-  auto gload = [&](int k0) {
-    const bool kin = k0 + lc * 16 < g.K;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t oa = (kin && voff_a[i] != kOutOfRange) ? voff_a[i] + k0 : kOutOfRange;
-      const uint32_t ow = (kin && voff_w[i] != kOutOfRange) ? voff_w[i] + k0 : kOutOfRange;
-      sa_regs[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)oa, 0, 0);
-      sw_regs[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)ow, 0, 0);
-    }
-  };
-  auto lstore = [&](int stage) {
+  const int dchunk_k = (dphys ^ drow_in_blk) * 16;  // row & 7 == drow_in_blk
+  auto dma = [&](int stage, int k0, bool step_valid) {
+    const bool kin = step_valid && k0 + dchunk_k < g.K;
     uint8_t* As = smem + stage * kStageBytes;
     uint8_t* Ws = As + kOperandBytes;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int row = i * 32 + lrow0;
-      *reinterpret_cast<v4i*>(As + lds_off(row, lc)) = sa_regs[i];
-      *reinterpret_cast<v4i*>(Ws + lds_off(row, lc)) = sw_regs[i];
+      const int blk = __builtin_amdgcn_readfirstlane(wave * 8 + i);
+      const uint32_t oa = (kin && dvoff_a[i] != kOutOfRange) ? dvoff_a[i] + k0 : kOutOfRange;
+      const uint32_t ow = (kin && dvoff_w[i] != kOutOfRange) ? dvoff_w[i] + k0 : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(As + blk * 1024), 16,
+                                               (int)oa, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void*)(Ws + blk * 1024), 16,
+                                               (int)ow, 0, 0, 0);
     }
   };
 
@@ -152,26 +152,34 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
   const int frow = lane & 31;          // operand row within a 32-row block
   const int fchunk = (lane >> 5) * 2;  // first of the lane's two chunks
 
-  gload(0);
-  lstore(0);
+  dma(0, 0, true);
   for (int kt = 0; kt < KT; ++kt) {
-    __syncthreads();
-    if (kt + 1 < KT) gload((kt + 1) * BK);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's loads for stage kt landed
+    __syncthreads();                       // ... and every other wave's
+    // next stage (an all-zero load into the idle buffer after the last
+    // step, which keeps the loop body one basic block for the scheduler)
+    dma((kt + 1) & 1, (kt + 1) * BK, kt + 1 < KT);
     const uint8_t* As = smem + (kt & 1) * kStageBytes;
     const uint8_t* Ws = As + kOperandBytes;
+    // all fragments of this k step first (both 64-wide halves), so the
+    // second half's LDS latency hides under the first half's products
+    v8i wf[2][4], af[2][4];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      v8i wf[4], af[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wf[i] = read_frag(Ws, wn * 128 + i * 32 + frow, ks * 4 + fchunk);
+      for (int i = 0; i < 4; ++i) wf[ks][i] = read_frag(Ws, wn * 128 + i * 32 + frow, ks * 4 + fchunk);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) af[j] = read_frag(As, wm * 128 + j * 32 + frow, ks * 4 + fchunk);
+      for (int j = 0; j < 4; ++j) af[ks][j] = read_frag(As, wm * 128 + j * 32 + frow, ks * 4 + fchunk);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
       if constexpr (!EXACT) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[i], af[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[ks][i], af[ks][j], acc[i][j], 0, 0, 0,
+                                                                         0, 0, 0);
       } else {
         // the lane's 32 k-values in four slices of 8 (same slicing for both
         // operands), one bf16 32x32x16 product per slice
@@ -179,9 +187,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
         for (int t = 0; t < 4; ++t) {
           bf16x8 wb[4], ab[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) wb[i] = slice_bf16(wf[i], t);
+          for (int i = 0; i < 4; ++i) wb[i] = slice_bf16(wf[ks][i], t);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) ab[j] = slice_bf16(af[j], t);
+          for (int j = 0; j < 4; ++j) ab[j] = slice_bf16(af[ks][j], t);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -190,7 +198,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
         }
       }
     }
-    if (kt + 1 < KT) lstore((kt + 1) & 1);
+    if constexpr (!EXACT) {
+      // issue order: the first half's 16 LDS reads, then one product per
+      // LDS read of the second half, then one product per load of the next
+      // stage, then the rest
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+    }
   }
 
   // ---- epilogue.  acc[i][j] = D[n][m] for the 32x32 block (i: n, j: m):
@@ -244,10 +267,11 @@ bool gemm_mfma_supported(const GemmArgs& g) {
 
 hipError_t launch_gemm_mfma(const GemmArgs& g, bool fp8_accumulate, hipStream_t stream) {
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  const unsigned grid = (unsigned)(tiles_m * tiles_n);
   if (fp8_accumulate)
-    gemm_mfma_kernel<false><<<(unsigned)(tiles_m * tiles_n), kThreads, 0, stream>>>(g, tiles_m, tiles_n);
+    gemm_mfma_kernel<false><<<grid, kThreads, 0, stream>>>(g, tiles_m, tiles_n);
   else
-    gemm_mfma_kernel<true><<<(unsigned)(tiles_m * tiles_n), kThreads, 0, stream>>>(g, tiles_m, tiles_n);
+    gemm_mfma_kernel<true><<<grid, kThreads, 0, stream>>>(g, tiles_m, tiles_n);
   return hipGetLastError();
 }
 

@@ -15,23 +15,29 @@
 // bf16 instruction v_mfma_f32_16x16x32_bf16, whose sums keep fp32-class
 // precision.  HBM traffic is unchanged: one byte per weight.
 //
-// Lane l holds row (l % 16) of each operand and 32 k-values of it per
-// 128-wide k step, and both operands use the same lane/element -> k
-// assignment, so products pair matching k whatever order the hardware sums
-// in.  Lane group g = l / 16 takes bytes [16g, 16g+16) and
-// [64+16g, 64+16g+16) of each 128-byte k step: every 16-byte load
-// instruction then reads 64 contiguous bytes of each of 16 rows.
+// Memory access: one 16-byte load instruction of a wave covers 4 rows x
+// 256 contiguous bytes (measured on MI355X: 16 rows x 64 bytes per
+// instruction streams at about half the rate).  The matrix cores want lane l
+// to hold row (l % 16) instead, so each wave transposes its 16 x 256-byte
+// step through a private, XOR-swizzled LDS buffer (conflict-free on both
+// the write and the read side), for the weight and for the activation rows.
+// Lane l then holds row (l % 16) of each operand and, per 128-wide k half,
+// bytes [16g, 16g+16) and [64+16g, 64+16g+16) with g = l / 16; both operands
+// use the same lane/element -> k assignment, so products pair matching k
+// whatever order the hardware sums in.
 //
-// The waves of a workgroup split the k steps (interleaved, so the group
-// reads adjacent 128-byte blocks of a row together) and are summed through
-// LDS in a fixed order, so results do not depend on timing.  The rescale
+// The waves of a workgroup split K into contiguous ranges of 256-byte steps,
+// keep two steps of loads in flight, and are summed through LDS in a fixed
+// order, so results do not depend on timing.  The rescale
 // epilogue out = acc * (s_a * s_w[n]) + bias[n] -> bf16 is applied in the
 // store ("[Kernel] Implement fallback for FP8 channelwise using
 // torch._scaled_mm", description: the channelwise rescale follows the
 // per-tensor GEMM; fused here instead of a separate pass).
 //
-// Larger M runs the same kernel over a grid of 16-row blocks of M; that is
-// the fallback for layouts the matrix-core GEMM does not take.
+// Larger M runs the same kernels over a grid of 16-row blocks of M; that is
+// the fallback for layouts the matrix-core GEMM does not take.  Layouts that
+// are not 16-byte aligned (or K % 16 != 0) use a byte-granular variant that
+// loads each lane's 32 bytes directly in the matrix-core layout.
 
 #include "device_common.h"
 #include "internal.h"
@@ -98,31 +104,11 @@ __device__ __forceinline__ v4f mfma_e4m3_as_bf16(v8i wf, v8i af, v4f acc) {
   return acc;
 }
 
-template <int NW, int U, bool VEC>
-__global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(GemmArgs g) {
-  __shared__ float red[NW][4][64];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int r = lane & 15, grp = lane >> 4;
-  const int n0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
-  const bool n_ok = n0 + r < g.N, m_ok = m0 + r < g.M;
-  const uint8_t* wrow = g.w + (int64_t)(n_ok ? n0 + r : 0) * g.ldw;
-  const uint8_t* arow = g.a + (int64_t)(m_ok ? m0 + r : 0) * g.lda;
-  const int ks = (g.K + 127) >> 7;
-
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = wave; s0 < ks; s0 += NW * U) {
-    v8i wf[U], af[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int s = s0 + u * NW;
-      wf[u] = load_frag<VEC>(wrow, s * 128, grp, g.K, n_ok && s < ks);
-      af[u] = load_frag<VEC>(arow, s * 128, grp, g.K, m_ok && s < ks);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) acc = mfma_e4m3_as_bf16(wf[u], af[u], acc);
-  }
-
+// Sum the waves' partial tiles through LDS in wave order and apply the
+// rescale epilogue.  acc holds D[n][m] for n = n0 + 4 * (lane / 16) + i and
+// m = m0 + lane % 16.
+__device__ __forceinline__ void reduce_and_store(const GemmArgs& g, v4f acc, float (*red)[4][64], int nw,
+                                                 int wave, int lane, int n0, int m0) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) red[wave][i][lane] = acc[i];
   __syncthreads();
@@ -131,14 +117,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float t = red[0][i][lane];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) t += red[w][i][lane];
+    for (int w = 1; w < nw; ++w) t += red[w][i][lane];
     sum[i] = t;
   }
-
-  // Result layout: lane holds output row m = m0 + (lane % 16) and the four
-  // consecutive columns n = n0 + 4 * (lane / 16) + i.
-  const int m = m0 + r;
+  const int grp = lane >> 4;
+  const int m = m0 + (lane & 15);
   if (m >= g.M) return;
   const int nb = n0 + 4 * grp;
   const float sa = *g.s_a;
@@ -165,33 +148,158 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(GemmArgs g) {
   }
 }
 
-template <int NW, bool VEC>
-hipError_t launch_nw(const GemmArgs& g, dim3 grid, hipStream_t stream) {
+__device__ __forceinline__ v8i cat8(v4i lo, v4i hi) {
+  v8i f;
+  f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
+  f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+  return f;
+}
+
+// Aligned layouts: rows 16-byte aligned and K % 16 == 0, so every 16-byte
+// chunk lies wholly inside or wholly outside [0, K).
+// Launched with blockDim.x = 64 * nw (nw <= kMaxWaves) and
+// skinny_lds_bytes(nw) bytes of dynamic LDS: per wave a 2 x 4 KiB staging
+// buffer, then the nw x 1 KiB reduction area.
+constexpr int kMaxWaves = 8;
+constexpr int kStageBytesPerWave = 2 * 16 * 256;
+
+inline size_t skinny_lds_bytes(int nw) { return (size_t)nw * (kStageBytesPerWave + 4 * 64 * sizeof(float)); }
+
+template <int P>
+__global__ __launch_bounds__(kMaxWaves * 64) void gemm_skinny_kernel(GemmArgs g) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
+  const int NW = blockDim.x >> 6;
+  uint8_t (*stage)[2][16 * 256] = reinterpret_cast<uint8_t (*)[2][16 * 256]>(dyn_lds);
+  float (*red)[4][64] = reinterpret_cast<float (*)[4][64]>(dyn_lds + NW * kStageBytesPerWave);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 15, grp = lane >> 4;
+  const int n0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
+  const int steps = (g.K + 255) >> 8;
+  const int per = (steps + NW - 1) / NW;
+  const int s_begin = min(wave * per, steps), s_end = min(s_begin + per, steps);
+  // load mapping: instruction j covers rows 4j + lane/16, bytes 16 * (lane % 16)
+  const int lr = lane >> 4, lc = (lane & 15) * 16;
+  const uint8_t* wp[4];
+  const uint8_t* ap[4];
+  bool wok[4], aok[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + 4 * j + lr, m = m0 + 4 * j + lr;
+    wok[j] = n < g.N;
+    aok[j] = m < g.M;
+    wp[j] = g.w + (int64_t)(wok[j] ? n : 0) * g.ldw + lc;
+    ap[j] = g.a + (int64_t)(aok[j] ? m : 0) * g.lda + lc;
+  }
+  uint8_t* LW = stage[wave][0];
+  uint8_t* LA = stage[wave][1];
+  const int swz_w = (lane & 15);  // chunk written by this lane (before the XOR)
+
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = s_begin; s < s_end; s += P) {
+    v4i wv[P][4], av[P][4];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int k0 = (s + p) * 256;
+      const bool kin = s + p < s_end && k0 + lc < g.K;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        wv[p][j] = (kin && wok[j]) ? *reinterpret_cast<const v4i*>(wp[j] + k0) : v4i{0, 0, 0, 0};
+        av[p][j] = (kin && aok[j]) ? *reinterpret_cast<const v4i*>(ap[j] + k0) : v4i{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      if (s + p >= s_end) break;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 4 * j + lr;
+        *reinterpret_cast<v4i*>(LW + row * 256 + ((swz_w ^ row) << 4)) = wv[p][j];
+        *reinterpret_cast<v4i*>(LA + row * 256 + ((swz_w ^ row) << 4)) = av[p][j];
+      }
+      // the same wave reads what its other lanes wrote: LDS operations of a
+      // wave complete in order, so waiting for them suffices
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int c0 = t * 8 + grp, c1 = t * 8 + 4 + grp;
+        const v4i wlo = *reinterpret_cast<const v4i*>(LW + r * 256 + ((c0 ^ r) << 4));
+        const v4i whi = *reinterpret_cast<const v4i*>(LW + r * 256 + ((c1 ^ r) << 4));
+        const v4i alo = *reinterpret_cast<const v4i*>(LA + r * 256 + ((c0 ^ r) << 4));
+        const v4i ahi = *reinterpret_cast<const v4i*>(LA + r * 256 + ((c1 ^ r) << 4));
+        acc = mfma_e4m3_as_bf16(cat8(wlo, whi), cat8(alo, ahi), acc);
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  reduce_and_store(g, acc, red, NW, wave, lane, n0, m0);
+}
+
+template <int NW, int U, bool VEC>
+__global__ __launch_bounds__(NW * 64) void gemm_skinny_generic_kernel(GemmArgs g) {
+  __shared__ float red[NW][4][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 15, grp = lane >> 4;
+  const int n0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
+  const bool n_ok = n0 + r < g.N, m_ok = m0 + r < g.M;
+  const uint8_t* wrow = g.w + (int64_t)(n_ok ? n0 + r : 0) * g.ldw;
+  const uint8_t* arow = g.a + (int64_t)(m_ok ? m0 + r : 0) * g.lda;
+  const int ks = (g.K + 127) >> 7;
+
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = wave; s0 < ks; s0 += NW * U) {
+    v8i wf[U], af[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * NW;
+      wf[u] = load_frag<VEC>(wrow, s * 128, grp, g.K, n_ok && s < ks);
+      af[u] = load_frag<VEC>(arow, s * 128, grp, g.K, m_ok && s < ks);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc = mfma_e4m3_as_bf16(wf[u], af[u], acc);
+  }
+
+  reduce_and_store(g, acc, red, NW, wave, lane, n0, m0);
+}
+
+template <int NW>
+hipError_t launch_generic(const GemmArgs& g, dim3 grid, hipStream_t stream) {
   constexpr int U = NW >= 16 ? 4 : 8;  // 16 waves leave 128 VGPRs per lane
-  gemm_skinny_kernel<NW, U, VEC><<<grid, NW * 64, 0, stream>>>(g);
+  gemm_skinny_generic_kernel<NW, U, false><<<grid, NW * 64, 0, stream>>>(g);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm_skinny(const GemmArgs& g, hipStream_t stream) {
-  const bool vec = ((uintptr_t)g.a % 16 == 0) && ((uintptr_t)g.w % 16 == 0) && (g.lda % 16 == 0) &&
-                   (g.ldw % 16 == 0) && (g.K % 16 == 0);
+  const bool aligned = ((uintptr_t)g.a % 16 == 0) && ((uintptr_t)g.w % 16 == 0) && (g.lda % 16 == 0) &&
+                       (g.ldw % 16 == 0) && (g.K % 16 == 0);
   const int64_t tiles_n = (g.N + 15) / 16, tiles_m = (g.M + 15) / 16;
   dim3 grid((unsigned)tiles_n, (unsigned)tiles_m);
+  if (aligned) {
+    // 8 waves for long K (more bytes in flight per workgroup), else 4
+    // dynamic LDS above 64 KiB must be allowed once per process
+    static const hipError_t lds_attr = hipFuncSetAttribute(
+        (const void*)gemm_skinny_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)skinny_lds_bytes(kMaxWaves));
+    if (lds_attr != hipSuccess) return lds_attr;
+    const int nw = (g.K + 255) / 256 >= 32 ? 8 : 4;
+    gemm_skinny_kernel<2><<<grid, nw * 64, skinny_lds_bytes(nw), stream>>>(g);
+    return hipGetLastError();
+  }
   const int64_t tiles = tiles_n * tiles_m;
   const int ks = (g.K + 127) / 128;
-  // More waves per workgroup when there are few workgroups, so that enough
-  // weight bytes are in flight to cover HBM latency; never more waves than
-  // k steps.
   int nw = tiles >= 256 ? 4 : (tiles >= 128 ? 8 : 16);
   while (nw > 1 && nw > ks) nw >>= 1;
   switch (nw) {
-    case 16: return vec ? launch_nw<16, true>(g, grid, stream) : launch_nw<16, false>(g, grid, stream);
-    case 8: return vec ? launch_nw<8, true>(g, grid, stream) : launch_nw<8, false>(g, grid, stream);
-    case 4: return vec ? launch_nw<4, true>(g, grid, stream) : launch_nw<4, false>(g, grid, stream);
-    case 2: return vec ? launch_nw<2, true>(g, grid, stream) : launch_nw<2, false>(g, grid, stream);
-    default: return vec ? launch_nw<1, true>(g, grid, stream) : launch_nw<1, false>(g, grid, stream);
+    case 16: return launch_generic<16>(g, grid, stream);
+    case 8: return launch_generic<8>(g, grid, stream);
+    case 4: return launch_generic<4>(g, grid, stream);
+    case 2: return launch_generic<2>(g, grid, stream);
+    default: return launch_generic<1>(g, grid, stream);
   }
 }
 

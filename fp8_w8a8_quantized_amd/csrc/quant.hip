@@ -3,12 +3,17 @@
 // Dynamic per-tensor quantization ("Prototype FP8Linear W8A8 runtime
 // quantization", opening post: activations are quantized per call): the
 // scale is amax/448, so amax needs the whole tensor before any code can be
-// written.  Small tensors (decode activations) run in one workgroup that
-// reads the tensor, reduces, and quantizes the now cache-resident tensor.
-// Large tensors (prefill) run two launches on the same stream: per-block
-// maxima into the workspace, then every block folds those maxima (a few KiB,
-// from L2) into the scale and quantizes its share.  No atomics, so results
-// and timing are deterministic, and the workspace needs no reset.
+// written.
+//   * Small tensors (decode activations, up to 256 Ki elements): one launch
+//     of up to 32 workgroups.  Every workgroup reduces the whole tensor
+//     itself (at most 512 KiB, served by L2 after the first touch), so no
+//     workgroup waits for another, then quantizes only its own share.
+//   * Large tensors (prefill): two launches on the same stream -- per-block
+//     maxima into the workspace, then every block folds those maxima (a few
+//     KiB, from L2) into the scale and quantizes its share.
+// No atomics and no inter-workgroup waiting: results and timing are
+// deterministic and the workspace needs no reset.  Each thread keeps
+// several 16-byte loads in flight (kUnroll), which is what HBM needs.
 //
 // Rows are handled as units of 8 elements (16 bytes of bf16 in, 8 bytes of
 // e4m3fn out).  The vector path needs 16-byte aligned input rows and 8-byte
@@ -31,49 +36,101 @@ struct QuantArgs {
   bool vec;  // aligned layout: 16-byte input rows, 8-byte output rows
 };
 
-__device__ __forceinline__ uint32_t unit_absmax(const QuantArgs& a, uint32_t u) {
-  const uint32_t r = fastdiv(u, a.div_units);
-  const uint32_t c0 = (u - r * a.units_per_row) * 8;
-  const uint16_t* row = a.x + (int64_t)r * a.ld_x;
-  if (a.vec && c0 + 8 <= a.cols) {
-    return absmax_bits8(*reinterpret_cast<const v4i*>(row + c0));
-  }
-  uint32_t m = 0;
-  for (uint32_t c = c0; c < c0 + 8 && c < a.cols; ++c) m = max(m, (uint32_t)row[c] & 0x7fffu);
-  return m;
+constexpr int kUnroll = 4;
+
+__device__ __forceinline__ bool unit_is_vector(const QuantArgs& a, uint32_t c0) {
+  return a.vec && c0 + 8 <= a.cols;
 }
 
-__device__ __forceinline__ void unit_quant(const QuantArgs& a, uint32_t u, float s) {
-  const uint32_t r = fastdiv(u, a.div_units);
-  const uint32_t c0 = (u - r * a.units_per_row) * 8;
+__device__ __forceinline__ void unit_coords(const QuantArgs& a, uint32_t u, uint32_t& r, uint32_t& c0) {
+  r = fastdiv(u, a.div_units);
+  c0 = (u - r * a.units_per_row) * 8;
+}
+
+__device__ __forceinline__ v4i unit_load(const QuantArgs& a, uint32_t r, uint32_t c0) {
   const uint16_t* row = a.x + (int64_t)r * a.ld_x;
+  if (unit_is_vector(a, c0)) return *reinterpret_cast<const v4i*>(row + c0);
+  uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (uint32_t c = c0; c < c0 + 8 && c < a.cols; ++c) h[c - c0] = row[c];
+  v4i v;
+  v[0] = (int)(h[0] | (h[1] << 16)); v[1] = (int)(h[2] | (h[3] << 16));
+  v[2] = (int)(h[4] | (h[5] << 16)); v[3] = (int)(h[6] | (h[7] << 16));
+  return v;  // missing elements are +0 and do not change the max
+}
+
+__device__ __forceinline__ void unit_store(const QuantArgs& a, uint32_t r, uint32_t c0, v4i x, float s) {
   uint8_t* qrow = a.q + (int64_t)r * a.ld_q;
-  if (a.vec && c0 + 8 <= a.cols) {
-    uint2 v = quant8(*reinterpret_cast<const v4i*>(row + c0), s);
+  const uint2 v = quant8(x, s);
+  if (unit_is_vector(a, c0)) {
     *reinterpret_cast<uint2*>(qrow + c0) = v;
     return;
   }
-  for (uint32_t c = c0; c < c0 + 8 && c < a.cols; ++c)
-    qrow[c] = (uint8_t)quant1(bf16_to_f32(row[c]), s);
+  for (uint32_t c = c0; c < c0 + 8 && c < a.cols; ++c) {
+    const uint32_t w = (c - c0) < 4 ? v.x : v.y;
+    qrow[c] = (uint8_t)(w >> (8 * ((c - c0) & 3)));
+  }
 }
 
-// One workgroup: amax, scale, quantize.
-__global__ __launch_bounds__(1024) void quant_dynamic_single_kernel(QuantArgs a, float* scale_out) {
-  __shared__ uint32_t red[16];
+// max |x| bits over units u0, u0 + stride, ... < u1, UNROLL loads in flight
+template <int UNROLL = kUnroll>
+__device__ __forceinline__ uint32_t absmax_range(const QuantArgs& a, uint32_t u0, uint32_t u1, uint32_t stride) {
   uint32_t m = 0;
-  for (uint32_t u = threadIdx.x; u < a.total_units; u += blockDim.x) m = max(m, unit_absmax(a, u));
+  for (uint32_t u = u0; u < u1; u += stride * UNROLL) {
+    v4i v[UNROLL];
+#pragma unroll
+    for (int i = 0; i < UNROLL; ++i) {
+      const uint32_t uu = u + i * stride;
+      v[i] = v4i{0, 0, 0, 0};
+      if (uu < u1) {
+        uint32_t r, c0;
+        unit_coords(a, uu, r, c0);
+        v[i] = unit_load(a, r, c0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < UNROLL; ++i) m = max(m, absmax_bits8(v[i]));
+  }
+  return m;
+}
+
+__device__ __forceinline__ void quant_range(const QuantArgs& a, uint32_t u0, uint32_t u1, uint32_t stride, float s) {
+  for (uint32_t u = u0; u < u1; u += stride * kUnroll) {
+    v4i v[kUnroll];
+    uint32_t r[kUnroll], c0[kUnroll];
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+      const uint32_t uu = u + i * stride;
+      r[i] = 0; c0[i] = 0; v[i] = v4i{0, 0, 0, 0};
+      if (uu < u1) {
+        unit_coords(a, uu, r[i], c0[i]);
+        v[i] = unit_load(a, r[i], c0[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i)
+      if (u + i * stride < u1) unit_store(a, r[i], c0[i], v[i], s);
+  }
+}
+
+// Small tensors, one launch: every workgroup reduces the whole tensor (1024
+// threads x 8 loads in flight = 128 KiB per round trip), then quantizes
+// units [blockIdx.x * per, ...).  Workgroup 0 writes the scale.
+constexpr int kSmallThreads = 1024;
+__global__ __launch_bounds__(kSmallThreads) void quant_dynamic_small_kernel(QuantArgs a, uint32_t per,
+                                                                            float* scale_out) {
+  __shared__ uint32_t red[16];
+  uint32_t m = absmax_range<8>(a, threadIdx.x, a.total_units, blockDim.x);
   m = block_max_u32(m, red);
   const float s = scale_from_amax(bf16_to_f32(m));
-  if (threadIdx.x == 0) *scale_out = s;
-  for (uint32_t u = threadIdx.x; u < a.total_units; u += blockDim.x) unit_quant(a, u, s);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
+  const uint32_t u0 = blockIdx.x * per, u1 = min(u0 + per, a.total_units);
+  quant_range(a, u0 + threadIdx.x, u1, blockDim.x, s);
 }
 
 // Launch 1 of 2: per-block maxima of |x| (as bf16 magnitude bits).
 __global__ __launch_bounds__(256) void absmax_partial_kernel(QuantArgs a, uint32_t* partial) {
   __shared__ uint32_t red[16];
-  uint32_t m = 0;
-  for (uint32_t u = blockIdx.x * blockDim.x + threadIdx.x; u < a.total_units; u += gridDim.x * blockDim.x)
-    m = max(m, unit_absmax(a, u));
+  uint32_t m = absmax_range(a, blockIdx.x * blockDim.x + threadIdx.x, a.total_units, gridDim.x * blockDim.x);
   m = block_max_u32(m, red);
   if (threadIdx.x == 0) partial[blockIdx.x] = m;
 }
@@ -87,14 +144,12 @@ __global__ __launch_bounds__(256) void quant_from_partial_kernel(QuantArgs a, co
   m = block_max_u32(m, red);
   const float s = scale_from_amax(bf16_to_f32(m));
   if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
-  for (uint32_t u = blockIdx.x * blockDim.x + threadIdx.x; u < a.total_units; u += gridDim.x * blockDim.x)
-    unit_quant(a, u, s);
+  quant_range(a, blockIdx.x * blockDim.x + threadIdx.x, a.total_units, gridDim.x * blockDim.x, s);
 }
 
 __global__ __launch_bounds__(256) void quant_static_kernel(QuantArgs a, const float* scale) {
   const float s = *scale;
-  for (uint32_t u = blockIdx.x * blockDim.x + threadIdx.x; u < a.total_units; u += gridDim.x * blockDim.x)
-    unit_quant(a, u, s);
+  quant_range(a, blockIdx.x * blockDim.x + threadIdx.x, a.total_units, gridDim.x * blockDim.x, s);
 }
 
 // One workgroup per row: the row's own amax and scale, then its codes.
@@ -102,12 +157,11 @@ __global__ __launch_bounds__(256) void quant_per_row_kernel(QuantArgs a, float* 
   __shared__ uint32_t red[16];
   const uint32_t r = blockIdx.x;
   const uint32_t u0 = r * a.units_per_row, u1 = u0 + a.units_per_row;
-  uint32_t m = 0;
-  for (uint32_t u = u0 + threadIdx.x; u < u1; u += blockDim.x) m = max(m, unit_absmax(a, u));
+  uint32_t m = absmax_range(a, u0 + threadIdx.x, u1, blockDim.x);
   m = block_max_u32(m, red);
   const float s = scale_from_amax(bf16_to_f32(m));
   if (threadIdx.x == 0) scales_out[r] = s;
-  for (uint32_t u = u0 + threadIdx.x; u < u1; u += blockDim.x) unit_quant(a, u, s);
+  quant_range(a, u0 + threadIdx.x, u1, blockDim.x, s);
 }
 
 __global__ void write_scale_kernel(float* scale_out, float v) { *scale_out = v; }
@@ -132,11 +186,12 @@ QuantArgs make_args(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
   return a;
 }
 
-constexpr uint32_t kPartialBlocks = 1024;       // max blocks of the two-launch path
-constexpr uint32_t kSingleBlockUnits = 1u << 13;  // <= 64 Ki elements: one workgroup
+constexpr uint32_t kPartialBlocks = 1024;         // max blocks of the two-launch path
+constexpr uint32_t kSmallUnits = 1u << 15;        // <= 256 Ki elements (512 KiB): one launch
+constexpr uint32_t kSmallUnitsPerBlock = 1024;    // quantize share of one block: 1 unit per thread
 
-uint32_t grid_for_units(uint32_t units, uint32_t cap) {
-  uint32_t g = (units + 255) / 256;
+uint32_t grid_for_units(uint32_t units, uint32_t per_block, uint32_t cap) {
+  uint32_t g = (units + per_block - 1) / per_block;
   return g < 1 ? 1 : (g > cap ? cap : g);
 }
 
@@ -152,16 +207,18 @@ hipError_t launch_quant_dynamic(const uint16_t* x, int64_t rows, int64_t cols, i
     return hipGetLastError();
   }
   QuantArgs a = make_args(x, rows, cols, ld_x, q, ld_q);
-  if (a.total_units <= kSingleBlockUnits) {
-    quant_dynamic_single_kernel<<<1, 1024, 0, stream>>>(a, scale_out);
+  if (a.total_units <= kSmallUnits) {
+    const uint32_t grid = grid_for_units(a.total_units, kSmallUnitsPerBlock, 32);
+    const uint32_t per = (a.total_units + grid - 1) / grid;
+    quant_dynamic_small_kernel<<<grid, kSmallThreads, 0, stream>>>(a, per, scale_out);
     return hipGetLastError();
   }
   uint32_t* partial = static_cast<uint32_t*>(workspace);
-  const uint32_t grid = grid_for_units(a.total_units, kPartialBlocks);
+  const uint32_t grid = grid_for_units(a.total_units, 256 * kUnroll, kPartialBlocks);
   absmax_partial_kernel<<<grid, 256, 0, stream>>>(a, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const uint32_t grid2 = grid_for_units(a.total_units, 4096);
+  const uint32_t grid2 = grid_for_units(a.total_units, 256 * kUnroll, 8192);
   quant_from_partial_kernel<<<grid2, 256, 0, stream>>>(a, partial, grid, scale_out);
   return hipGetLastError();
 }
@@ -170,7 +227,7 @@ hipError_t launch_quant_static(const uint16_t* x, int64_t rows, int64_t cols, in
                                uint8_t* q, int64_t ld_q, hipStream_t stream) {
   if (rows == 0 || cols == 0) return hipSuccess;
   QuantArgs a = make_args(x, rows, cols, ld_x, q, ld_q);
-  quant_static_kernel<<<grid_for_units(a.total_units, 4096), 256, 0, stream>>>(a, scale);
+  quant_static_kernel<<<grid_for_units(a.total_units, 256 * kUnroll, 8192), 256, 0, stream>>>(a, scale);
   return hipGetLastError();
 }
 
