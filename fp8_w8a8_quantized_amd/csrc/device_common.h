@@ -25,11 +25,12 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
 }
 
 // float32 -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN).
+// Branch-free: both results are formed and one is selected.
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet_nan = (u >> 16) | 0x40u;
+  return (u & 0x7fffffffu) > 0x7f800000u ? quiet_nan : rounded;
 }
 
 // Per-tensor scale from amax: amax / 448 correctly rounded in float32; an
