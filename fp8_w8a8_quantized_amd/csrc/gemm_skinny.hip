@@ -107,8 +107,27 @@ __device__ __forceinline__ v4f mfma_e4m3_as_bf16(v8i wf, v8i af, v4f acc) {
 // Sum the waves' partial tiles through LDS in wave order and apply the
 // rescale epilogue.  acc holds D[n][m] for n = n0 + 4 * (lane / 16) + i and
 // m = m0 + lane % 16.
+// The epilogue's per-column factors, loaded at kernel start so that their
+// memory latency overlaps the main loop instead of following it.
+struct EpiParams {
+  float sc[4], bs[4];
+};
+
+__device__ __forceinline__ EpiParams load_epi_params(const GemmArgs& g, int lane, int n0) {
+  EpiParams p;
+  const float sa = *g.s_a;
+  const int nb = n0 + 4 * (lane >> 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = min(nb + i, g.N - 1);
+    p.sc[i] = sa * (g.per_channel ? g.s_w[n] : g.s_w[0]);
+    p.bs[i] = g.bias ? bf16_to_f32(g.bias[n]) : 0.0f;
+  }
+  return p;
+}
+
 __device__ __forceinline__ void reduce_and_store(const GemmArgs& g, v4f acc, float (*red)[4][64], int nw,
-                                                 int wave, int lane, int n0, int m0) {
+                                                 int wave, int lane, int n0, int m0, const EpiParams& ep) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) red[wave][i][lane] = acc[i];
   __syncthreads();
@@ -124,17 +143,9 @@ __device__ __forceinline__ void reduce_and_store(const GemmArgs& g, v4f acc, flo
   const int m = m0 + (lane & 15);
   if (m >= g.M) return;
   const int nb = n0 + 4 * grp;
-  const float sa = *g.s_a;
   uint32_t o[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int n = nb + i;
-    if (n < g.N) {
-      const float sc = sa * (g.per_channel ? g.s_w[n] : g.s_w[0]);
-      const float b = g.bias ? bf16_to_f32(g.bias[n]) : 0.0f;
-      o[i] = f32_to_bf16_rne(__builtin_fmaf(sum[i], sc, b));
-    }
-  }
+  for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16_rne(__builtin_fmaf(sum[i], ep.sc[i], ep.bs[i]));
   uint16_t* orow = g.out + (int64_t)m * g.ldo;
   if (nb + 3 < g.N && ((uintptr_t)(orow + nb) % 8) == 0) {
     uint2 v;
@@ -195,6 +206,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemm_skinny_kernel(GemmArgs g)
   uint8_t* LA = stage[wave][1];
   const int swz_w = (lane & 15);  // chunk written by this lane (before the XOR)
 
+  const EpiParams ep = load_epi_params(g, lane, n0);
   v4f acc = {0.f, 0.f, 0.f, 0.f};
   for (int s = s_begin; s < s_end; s += P) {
     v4i wv[P][4], av[P][4];
@@ -234,7 +246,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemm_skinny_kernel(GemmArgs g)
       __builtin_amdgcn_wave_barrier();
     }
   }
-  reduce_and_store(g, acc, red, NW, wave, lane, n0, m0);
+  reduce_and_store(g, acc, red, NW, wave, lane, n0, m0, ep);
 }
 
 template <int NW, int U, bool VEC>
@@ -249,6 +261,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_generic_kernel(GemmArgs g
   const uint8_t* arow = g.a + (int64_t)(m_ok ? m0 + r : 0) * g.lda;
   const int ks = (g.K + 127) >> 7;
 
+  const EpiParams ep = load_epi_params(g, lane, n0);
   v4f acc = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = wave; s0 < ks; s0 += NW * U) {
     v8i wf[U], af[U];
@@ -262,7 +275,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_generic_kernel(GemmArgs g
     for (int u = 0; u < U; ++u) acc = mfma_e4m3_as_bf16(wf[u], af[u], acc);
   }
 
-  reduce_and_store(g, acc, red, NW, wave, lane, n0, m0);
+  reduce_and_store(g, acc, red, NW, wave, lane, n0, m0, ep);
 }
 
 template <int NW>

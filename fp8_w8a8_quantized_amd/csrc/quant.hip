@@ -7,7 +7,8 @@
 //   * Small tensors (decode activations, up to 256 Ki elements): one launch
 //     of up to 32 workgroups.  Every workgroup reduces the whole tensor
 //     itself (at most 512 KiB, served by L2 after the first touch), so no
-//     workgroup waits for another, then quantizes only its own share.
+//     workgroup waits for another, and quantizes only its own share, which
+//     it kept in registers from that pass.
 //   * Large tensors (prefill): two launches on the same stream -- per-block
 //     maxima into the workspace, then every block folds those maxima (a few
 //     KiB, from L2) into the scale and quantizes its share.
@@ -113,18 +114,45 @@ __device__ __forceinline__ void quant_range(const QuantArgs& a, uint32_t u0, uin
 }
 
 // Small tensors, one launch: every workgroup reduces the whole tensor (1024
-// threads x 8 loads in flight = 128 KiB per round trip), then quantizes
-// units [blockIdx.x * per, ...).  Workgroup 0 writes the scale.
+// threads, 8 loads of 16 bytes in flight each), keeping in registers the
+// slot it will quantize -- units blockIdx.x * 1024 + threadIdx.x -- so the
+// codes need no second read.  The grid has one workgroup per slot (at most
+// 32); workgroup 0 writes the scale.
 constexpr int kSmallThreads = 1024;
-__global__ __launch_bounds__(kSmallThreads) void quant_dynamic_small_kernel(QuantArgs a, uint32_t per,
-                                                                            float* scale_out) {
+constexpr int kSmallBatch = 8;
+__global__ __launch_bounds__(kSmallThreads) void quant_dynamic_small_kernel(QuantArgs a, float* scale_out) {
   __shared__ uint32_t red[16];
-  uint32_t m = absmax_range<8>(a, threadIdx.x, a.total_units, blockDim.x);
+  const uint32_t T = a.total_units;
+  const uint32_t slots = gridDim.x;
+  uint32_t m = 0;
+  v4i keep = {0, 0, 0, 0};
+  for (uint32_t j0 = 0; j0 < slots; j0 += kSmallBatch) {
+    v4i v[kSmallBatch];
+#pragma unroll
+    for (int i = 0; i < kSmallBatch; ++i) {
+      const uint32_t u = threadIdx.x + (j0 + i) * kSmallThreads;
+      v[i] = v4i{0, 0, 0, 0};
+      if (u < T) {
+        uint32_t r, c0;
+        unit_coords(a, u, r, c0);
+        v[i] = unit_load(a, r, c0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kSmallBatch; ++i) {
+      m = max(m, absmax_bits8(v[i]));
+      if (j0 + i == blockIdx.x) keep = v[i];
+    }
+  }
   m = block_max_u32(m, red);
   const float s = scale_from_amax(bf16_to_f32(m));
   if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
-  const uint32_t u0 = blockIdx.x * per, u1 = min(u0 + per, a.total_units);
-  quant_range(a, u0 + threadIdx.x, u1, blockDim.x, s);
+  const uint32_t u = threadIdx.x + blockIdx.x * kSmallThreads;
+  if (u < T) {
+    uint32_t r, c0;
+    unit_coords(a, u, r, c0);
+    unit_store(a, r, c0, keep, s);
+  }
 }
 
 // Launch 1 of 2: per-block maxima of |x| (as bf16 magnitude bits).
@@ -188,7 +216,6 @@ QuantArgs make_args(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
 
 constexpr uint32_t kPartialBlocks = 1024;         // max blocks of the two-launch path
 constexpr uint32_t kSmallUnits = 1u << 15;        // <= 256 Ki elements (512 KiB): one launch
-constexpr uint32_t kSmallUnitsPerBlock = 1024;    // quantize share of one block: 1 unit per thread
 
 uint32_t grid_for_units(uint32_t units, uint32_t per_block, uint32_t cap) {
   uint32_t g = (units + per_block - 1) / per_block;
@@ -208,9 +235,9 @@ hipError_t launch_quant_dynamic(const uint16_t* x, int64_t rows, int64_t cols, i
   }
   QuantArgs a = make_args(x, rows, cols, ld_x, q, ld_q);
   if (a.total_units <= kSmallUnits) {
-    const uint32_t grid = grid_for_units(a.total_units, kSmallUnitsPerBlock, 32);
-    const uint32_t per = (a.total_units + grid - 1) / grid;
-    quant_dynamic_small_kernel<<<grid, kSmallThreads, 0, stream>>>(a, per, scale_out);
+    // one workgroup per 1024-unit slot: at most kSmallUnits / 1024 = 32
+    const uint32_t grid = (a.total_units + kSmallThreads - 1) / kSmallThreads;
+    quant_dynamic_small_kernel<<<grid, kSmallThreads, 0, stream>>>(a, scale_out);
     return hipGetLastError();
   }
   uint32_t* partial = static_cast<uint32_t*>(workspace);
