@@ -18,6 +18,10 @@ Sources (page title, then the part of the page):
     (vLLM PR 6552), description: a channelwise (per output channel) weight
     scale is applied as a rescale after a per-tensor scaled GEMM.
 
+oracle.glue holds the steps between the linears of the chained-linears
+workload (residual add, RMS normalization, gated activation), which the pages
+do not define; its readings are stated there.
+
 Every function is pinned by tests marked ``not gpu`` to facts fixed outside
 itself (closed forms, the 256-pattern table, exhaustive bf16 sweeps, a library
 cast, int64 brute force).  The end-to-end model quality numbers on the pages
@@ -36,4 +40,12 @@ from .w8a8 import (  # noqa: F401
     scaled_mm,
     dequant_row_norms,
     to_bf16_rne,
+)
+from .glue import (  # noqa: F401
+    add_bf16,
+    rmsnorm,
+    silu_mul,
+    f32_to_bf16_bits,
+    f64_to_bf16_bits,
+    bf16_ulp_distance,
 )
