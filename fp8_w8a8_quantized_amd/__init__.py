@@ -33,6 +33,10 @@ SIGNATURES = {
     "fp8_quant_static": (_I, [_P, _I64, _I64, _I64, _P, _P, _I64, _P]),
     "fp8_quant_dynamic_per_row": (_I, [_P, _I64, _I64, _I64, _P, _I64, _P, _P]),
     "fp8_scaled_mm": (_I, [_P, _I64, _P, _I64, _P, _P, _I, _I, _P, _P, _I64, _I64, _I64, _I64, _P]),
+    "fp8_norm_quant_workspace_bytes": (ctypes.c_size_t, [_I64]),
+    "fp8_add_rmsnorm_quant_dynamic": (_I, [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, ctypes.c_float,
+                                           _P, _I64, _P, _I64, _P, _P, _P]),
+    "fp8_silu_mul_quant_dynamic": (_I, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _P, _P]),
 }
 
 _lib = None
@@ -158,3 +162,53 @@ def linear(x, w_q, s_w, per_channel, bias=None, workspace=None, accum="fp32"):
     """The W8A8 linear: dynamic activation quantization then scaled GEMM."""
     a_q, s_a = quant_dynamic(x, workspace=workspace)
     return scaled_mm(a_q, w_q, s_a, s_w, per_channel, bias, accum=accum)
+
+
+def norm_workspace(rows, device=None):
+    return torch.empty(int(lib().fp8_norm_quant_workspace_bytes(rows)), dtype=torch.uint8,
+                       device=device or "cuda")
+
+
+def add_rmsnorm_quant(h, delta=None, h_out=None, eps=1e-5, y_out=None, q=None, scale=None, workspace=None):
+    """Residual add (optional), unit-weight RMS normalization and dynamic
+    per-tensor quantization in one pass over h.
+
+    Returns (q uint8, scale float32 [1], h_out or None, y_out or None):
+    h_out receives bf16(h + delta) when delta is given; y_out, when given,
+    receives the normalized bf16 values that were quantized.
+    """
+    _mat(h, "h", torch.bfloat16)
+    rows, cols = h.shape
+    if delta is not None:
+        _mat(delta, "delta", torch.bfloat16)
+        h_out = torch.empty_like(h) if h_out is None else _mat(h_out, "h_out", torch.bfloat16)
+    if y_out is not None:
+        _mat(y_out, "y_out", torch.bfloat16)
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=h.device) if q is None else q
+    scale = torch.empty(1, dtype=torch.float32, device=h.device) if scale is None else scale
+    workspace = norm_workspace(rows, h.device) if workspace is None else workspace
+    _check(lib().fp8_add_rmsnorm_quant_dynamic(
+        _ptr(h), h.stride(0), _ptr(delta), delta.stride(0) if delta is not None else 0,
+        _ptr(h_out if delta is not None else None), h_out.stride(0) if delta is not None else 0,
+        rows, cols, ctypes.c_float(eps), _ptr(y_out), y_out.stride(0) if y_out is not None else 0,
+        _ptr(q), q.stride(0), _ptr(scale), _ptr(workspace), _stream()), "fp8_add_rmsnorm_quant_dynamic")
+    return q, scale, (h_out if delta is not None else None), y_out
+
+
+def silu_mul_quant(gu, y_out=None, q=None, scale=None, workspace=None):
+    """silu(gate) * up of a fused gate_up output [rows, 2 cols] (gate first),
+    quantized with a dynamic per-tensor scale.  Returns (q, scale, y_out)."""
+    _mat(gu, "gu", torch.bfloat16)
+    rows, two_cols = gu.shape
+    if two_cols % 2:
+        raise ValueError("gu must have an even number of columns (gate | up)")
+    cols = two_cols // 2
+    if y_out is not None:
+        _mat(y_out, "y_out", torch.bfloat16)
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=gu.device) if q is None else q
+    scale = torch.empty(1, dtype=torch.float32, device=gu.device) if scale is None else scale
+    workspace = new_workspace(gu.device) if workspace is None else workspace
+    _check(lib().fp8_silu_mul_quant_dynamic(_ptr(gu), gu.stride(0), rows, cols, _ptr(y_out),
+                                            y_out.stride(0) if y_out is not None else 0, _ptr(q), q.stride(0),
+                                            _ptr(scale), _ptr(workspace), _stream()), "fp8_silu_mul_quant_dynamic")
+    return q, scale, y_out

@@ -84,6 +84,51 @@ fp8_status fp8_quant_dynamic_per_row(const uint16_t* x_bf16, int64_t rows, int64
                     fn);
 }
 
+size_t fp8_norm_quant_workspace_bytes(int64_t rows) {
+  return fp8w8a8::norm_quant_workspace_bytes(rows < 0 ? 0 : rows);
+}
+
+fp8_status fp8_add_rmsnorm_quant_dynamic(const uint16_t* h_bf16, int64_t ld_h, const uint16_t* delta_bf16,
+                                         int64_t ld_delta, uint16_t* h_out_bf16, int64_t ld_h_out, int64_t rows,
+                                         int64_t cols, float eps, uint16_t* y_out_bf16, int64_t ld_y,
+                                         uint8_t* q_e4m3, int64_t ld_q, float* scale_out, void* workspace,
+                                         void* stream) {
+  const char* fn = "fp8_add_rmsnorm_quant_dynamic";
+  fp8_status st = check_quant(fn, h_bf16, rows, cols, ld_h, q_e4m3, ld_q);
+  if (st != FP8_OK) return st;
+  if (scale_out == nullptr) return fail(FP8_ERR_INVALID_ARG, "%s: null scale_out", fn);
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return fail(FP8_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", fn);
+  const bool work = rows > 0 && cols > 0;
+  if (work && workspace == nullptr) return fail(FP8_ERR_INVALID_ARG, "%s: null workspace", fn);
+  if (work && delta_bf16 != nullptr) {
+    if (h_out_bf16 == nullptr) return fail(FP8_ERR_INVALID_ARG, "%s: delta given but h_out is null", fn);
+    if (ld_delta < cols || ld_h_out < cols)
+      return fail(FP8_ERR_INVALID_ARG, "%s: ld_delta/ld_h_out smaller than cols", fn);
+  }
+  if (work && y_out_bf16 != nullptr && ld_y < cols) return fail(FP8_ERR_INVALID_ARG, "%s: ld_y smaller than cols", fn);
+  if (rows >= (1ll << 31)) return fail(FP8_ERR_UNSUPPORTED, "%s: too many rows", fn);
+  return hip_status(fp8w8a8::launch_add_rmsnorm_quant(h_bf16, ld_h, delta_bf16, ld_delta, h_out_bf16, ld_h_out, rows,
+                                                      cols, eps, y_out_bf16, ld_y, q_e4m3, ld_q, scale_out, workspace,
+                                                      static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+fp8_status fp8_silu_mul_quant_dynamic(const uint16_t* gu_bf16, int64_t ld_gu, int64_t rows, int64_t cols,
+                                      uint16_t* y_out_bf16, int64_t ld_y, uint8_t* q_e4m3, int64_t ld_q,
+                                      float* scale_out, void* workspace, void* stream) {
+  const char* fn = "fp8_silu_mul_quant_dynamic";
+  fp8_status st = check_quant(fn, gu_bf16, rows, cols, ld_gu, q_e4m3, ld_q);
+  if (st != FP8_OK) return st;
+  if (cols > 0 && ld_gu < 2 * cols) return fail(FP8_ERR_INVALID_ARG, "%s: ld_gu smaller than 2 * cols", fn);
+  if (scale_out == nullptr) return fail(FP8_ERR_INVALID_ARG, "%s: null scale_out", fn);
+  const bool work = rows > 0 && cols > 0;
+  if (work && workspace == nullptr) return fail(FP8_ERR_INVALID_ARG, "%s: null workspace", fn);
+  if (work && y_out_bf16 != nullptr && ld_y < cols) return fail(FP8_ERR_INVALID_ARG, "%s: ld_y smaller than cols", fn);
+  return hip_status(fp8w8a8::launch_silu_mul_quant(gu_bf16, ld_gu, rows, cols, y_out_bf16, ld_y, q_e4m3, ld_q,
+                                                   scale_out, workspace, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 fp8_status fp8_scaled_mm(const uint8_t* a_q, int64_t lda, const uint8_t* w_q, int64_t ldw, const float* s_a,
                          const float* s_w, fp8_scale_mode mode, fp8_accum_mode accum, const uint16_t* bias_bf16,
                          uint16_t* out_bf16, int64_t ldo, int64_t M, int64_t N, int64_t K, void* stream) {

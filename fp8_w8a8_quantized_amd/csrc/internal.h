@@ -14,6 +14,15 @@ hipError_t launch_quant_dynamic(const uint16_t* x, int64_t rows, int64_t cols, i
                                 int64_t ld_q, float* scale_out, void* workspace, hipStream_t stream);
 hipError_t launch_quant_static(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, const float* scale,
                                uint8_t* q, int64_t ld_q, hipStream_t stream);
+// Fused producers (chained-linears glue) + dynamic per-tensor quantization.
+size_t norm_quant_workspace_bytes(int64_t rows);
+hipError_t launch_add_rmsnorm_quant(const uint16_t* h, int64_t ld_h, const uint16_t* delta, int64_t ld_delta,
+                                    uint16_t* h_out, int64_t ld_h_out, int64_t rows, int64_t cols, float eps,
+                                    uint16_t* y_out, int64_t ld_y, uint8_t* q, int64_t ld_q, float* scale_out,
+                                    void* workspace, hipStream_t stream);
+hipError_t launch_silu_mul_quant(const uint16_t* gu, int64_t ld_gu, int64_t rows, int64_t cols, uint16_t* y_out,
+                                 int64_t ld_y, uint8_t* q, int64_t ld_q, float* scale_out, void* workspace,
+                                 hipStream_t stream);
 hipError_t launch_quant_per_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
                                 int64_t ld_q, float* scales_out, hipStream_t stream);
 

@@ -16,6 +16,13 @@
 // deterministic and the workspace needs no reset.  Each thread keeps
 // several 16-byte loads in flight (kUnroll), which is what HBM needs.
 //
+// The same machinery quantizes values produced on the fly (value sources,
+// below): the plain activations, a unit-weight RMS normalization of a
+// residual stream (after an optional residual add), or a gate-first
+// SiLU*mul.  Producer and quantization then share one pass over the input,
+// so the produced bf16 tensor never round-trips through memory; an optional
+// copy can still be written, by the pass that writes the codes.
+//
 // Rows are handled as units of 8 elements (16 bytes of bf16 in, 8 bytes of
 // e4m3fn out).  The vector path needs 16-byte aligned input rows and 8-byte
 // aligned output rows; a row's ragged end and unaligned layouts use
@@ -28,41 +35,27 @@ namespace fp8w8a8 {
 
 namespace {
 
+// The codes side of a quantization: where the e4m3 codes go and the unit
+// geometry (a unit is 8 consecutive columns of one row).
 struct QuantArgs {
-  const uint16_t* x;
   uint8_t* q;
-  int64_t ld_x, ld_q;
+  int64_t ld_q;
   uint32_t rows, cols, units_per_row, total_units;
   FastDivU32 div_units;
-  bool vec;  // aligned layout: 16-byte input rows, 8-byte output rows
+  bool vec_q;  // 8-byte aligned code rows
 };
 
 constexpr int kUnroll = 4;
-
-__device__ __forceinline__ bool unit_is_vector(const QuantArgs& a, uint32_t c0) {
-  return a.vec && c0 + 8 <= a.cols;
-}
 
 __device__ __forceinline__ void unit_coords(const QuantArgs& a, uint32_t u, uint32_t& r, uint32_t& c0) {
   r = fastdiv(u, a.div_units);
   c0 = (u - r * a.units_per_row) * 8;
 }
 
-__device__ __forceinline__ v4i unit_load(const QuantArgs& a, uint32_t r, uint32_t c0) {
-  const uint16_t* row = a.x + (int64_t)r * a.ld_x;
-  if (unit_is_vector(a, c0)) return *reinterpret_cast<const v4i*>(row + c0);
-  uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (uint32_t c = c0; c < c0 + 8 && c < a.cols; ++c) h[c - c0] = row[c];
-  v4i v;
-  v[0] = (int)(h[0] | (h[1] << 16)); v[1] = (int)(h[2] | (h[3] << 16));
-  v[2] = (int)(h[4] | (h[5] << 16)); v[3] = (int)(h[6] | (h[7] << 16));
-  return v;  // missing elements are +0 and do not change the max
-}
-
 __device__ __forceinline__ void unit_store(const QuantArgs& a, uint32_t r, uint32_t c0, v4i x, float s) {
   uint8_t* qrow = a.q + (int64_t)r * a.ld_q;
   const uint2 v = quant8(x, s);
-  if (unit_is_vector(a, c0)) {
+  if (a.vec_q && c0 + 8 <= a.cols) {
     *reinterpret_cast<uint2*>(qrow + c0) = v;
     return;
   }
@@ -72,9 +65,107 @@ __device__ __forceinline__ void unit_store(const QuantArgs& a, uint32_t r, uint3
   }
 }
 
+// 8 bf16 of a row starting at column c0 (columns past `cols` read as +0).
+__device__ __forceinline__ v4i load8_bf16(const uint16_t* row, uint32_t c0, uint32_t cols, bool vec) {
+  if (vec && c0 + 8 <= cols) return *reinterpret_cast<const v4i*>(row + c0);
+  uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (uint32_t c = c0; c < c0 + 8 && c < cols; ++c) h[c - c0] = row[c];
+  v4i v;
+  v[0] = (int)(h[0] | (h[1] << 16)); v[1] = (int)(h[2] | (h[3] << 16));
+  v[2] = (int)(h[4] | (h[5] << 16)); v[3] = (int)(h[6] | (h[7] << 16));
+  return v;
+}
+
+__device__ __forceinline__ void store8_bf16(uint16_t* row, uint32_t c0, uint32_t cols, bool vec, v4i v) {
+  if (vec && c0 + 8 <= cols) {
+    *reinterpret_cast<v4i*>(row + c0) = v;
+    return;
+  }
+  for (uint32_t c = c0; c < c0 + 8 && c < cols; ++c) {
+    const uint32_t w = (uint32_t)v[(c - c0) >> 1];
+    row[c] = (uint16_t)(((c - c0) & 1) ? (w >> 16) : (w & 0xffffu));
+  }
+}
+
+__device__ __forceinline__ float bf16_at(v4i v, int i) {
+  const uint32_t w = (uint32_t)v[i >> 1];
+  return bf16_to_f32((i & 1) ? (w >> 16) : (w & 0xffffu));
+}
+
+__device__ __forceinline__ v4i pack8_bf16(const float f[8]) {
+  v4i v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = (int)(f32_to_bf16_rne(f[2 * i]) | (f32_to_bf16_rne(f[2 * i + 1]) << 16));
+  return v;
+}
+
+// ---- value sources: the bf16 values a quantization encodes, per unit.
+// load() gives the unit's 8 values (columns past `cols` as +0); emit() may
+// write them out and is called once per unit, by the pass that writes the
+// unit's codes.
+
+// The activations themselves.
+struct PlainSrc {
+  const uint16_t* x;
+  int64_t ld;
+  bool vec;  // 16-byte aligned rows
+  __device__ __forceinline__ v4i load(const QuantArgs& a, uint32_t r, uint32_t c0) const {
+    return load8_bf16(x + (int64_t)r * ld, c0, a.cols, vec);
+  }
+  __device__ __forceinline__ void emit(const QuantArgs&, uint32_t, uint32_t, v4i) const {}
+};
+
+// Unit-weight RMS normalization: y = bf16(h * inv_rms[row]), inv_rms from
+// row_stats_kernel.
+struct NormSrc {
+  const uint16_t* h;
+  int64_t ld_h;
+  const float* inv_rms;
+  uint16_t* y;  // optional copy of the normalized values
+  int64_t ld_y;
+  bool vec_h, vec_y;
+  __device__ __forceinline__ v4i load(const QuantArgs& a, uint32_t r, uint32_t c0) const {
+    const v4i hv = load8_bf16(h + (int64_t)r * ld_h, c0, a.cols, vec_h);
+    const float g = inv_rms[r];
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = bf16_at(hv, i) * g;
+    return pack8_bf16(f);
+  }
+  __device__ __forceinline__ void emit(const QuantArgs& a, uint32_t r, uint32_t c0, v4i v) const {
+    if (y != nullptr) store8_bf16(y + (int64_t)r * ld_y, c0, a.cols, vec_y, v);
+  }
+};
+
+// Gated activation, gate half first: y = bf16(silu(g) * u) with
+// silu(g) = g / (1 + exp(-g)) in float32.
+struct SiluMulSrc {
+  const uint16_t* gu;  // row r: gate columns [0, cols), up columns [cols, 2 cols)
+  int64_t ld;
+  uint16_t* y;  // optional copy of the activated values
+  int64_t ld_y;
+  bool vec, vec_y;
+  __device__ __forceinline__ v4i load(const QuantArgs& a, uint32_t r, uint32_t c0) const {
+    const uint16_t* row = gu + (int64_t)r * ld;
+    const v4i gv = load8_bf16(row, c0, a.cols, vec);
+    const v4i uv = load8_bf16(row + a.cols, c0, a.cols, vec);
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float g = bf16_at(gv, i);
+      f[i] = g / (1.0f + expf(-g)) * bf16_at(uv, i);
+    }
+    return pack8_bf16(f);
+  }
+  __device__ __forceinline__ void emit(const QuantArgs& a, uint32_t r, uint32_t c0, v4i v) const {
+    if (y != nullptr) store8_bf16(y + (int64_t)r * ld_y, c0, a.cols, vec_y, v);
+  }
+};
+
 // max |x| bits over units u0, u0 + stride, ... < u1, UNROLL loads in flight
-template <int UNROLL = kUnroll>
-__device__ __forceinline__ uint32_t absmax_range(const QuantArgs& a, uint32_t u0, uint32_t u1, uint32_t stride) {
+template <class Src, int UNROLL = kUnroll>
+__device__ __forceinline__ uint32_t absmax_range(const QuantArgs& a, const Src& src, uint32_t u0, uint32_t u1,
+                                                 uint32_t stride) {
   uint32_t m = 0;
   for (uint32_t u = u0; u < u1; u += stride * UNROLL) {
     v4i v[UNROLL];
@@ -85,7 +176,7 @@ __device__ __forceinline__ uint32_t absmax_range(const QuantArgs& a, uint32_t u0
       if (uu < u1) {
         uint32_t r, c0;
         unit_coords(a, uu, r, c0);
-        v[i] = unit_load(a, r, c0);
+        v[i] = src.load(a, r, c0);
       }
     }
 #pragma unroll
@@ -94,7 +185,9 @@ __device__ __forceinline__ uint32_t absmax_range(const QuantArgs& a, uint32_t u0
   return m;
 }
 
-__device__ __forceinline__ void quant_range(const QuantArgs& a, uint32_t u0, uint32_t u1, uint32_t stride, float s) {
+template <class Src>
+__device__ __forceinline__ void quant_range(const QuantArgs& a, const Src& src, uint32_t u0, uint32_t u1,
+                                            uint32_t stride, float s) {
   for (uint32_t u = u0; u < u1; u += stride * kUnroll) {
     v4i v[kUnroll];
     uint32_t r[kUnroll], c0[kUnroll];
@@ -104,12 +197,15 @@ __device__ __forceinline__ void quant_range(const QuantArgs& a, uint32_t u0, uin
       r[i] = 0; c0[i] = 0; v[i] = v4i{0, 0, 0, 0};
       if (uu < u1) {
         unit_coords(a, uu, r[i], c0[i]);
-        v[i] = unit_load(a, r[i], c0[i]);
+        v[i] = src.load(a, r[i], c0[i]);
       }
     }
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i)
-      if (u + i * stride < u1) unit_store(a, r[i], c0[i], v[i], s);
+      if (u + i * stride < u1) {
+        src.emit(a, r[i], c0[i], v[i]);
+        unit_store(a, r[i], c0[i], v[i], s);
+      }
   }
 }
 
@@ -117,10 +213,12 @@ __device__ __forceinline__ void quant_range(const QuantArgs& a, uint32_t u0, uin
 // threads, 8 loads of 16 bytes in flight each), keeping in registers the
 // slot it will quantize -- units blockIdx.x * 1024 + threadIdx.x -- so the
 // codes need no second read.  The grid has one workgroup per slot (at most
-// 32); workgroup 0 writes the scale.
+// 32); workgroup 0 writes the scale.  Only for cheap sources: every
+// workgroup evaluates the source over the whole tensor.
 constexpr int kSmallThreads = 1024;
 constexpr int kSmallBatch = 8;
-__global__ __launch_bounds__(kSmallThreads) void quant_dynamic_small_kernel(QuantArgs a, float* scale_out) {
+template <class Src>
+__global__ __launch_bounds__(kSmallThreads) void quant_dynamic_small_kernel(QuantArgs a, Src src, float* scale_out) {
   __shared__ uint32_t red[16];
   const uint32_t T = a.total_units;
   const uint32_t slots = gridDim.x;
@@ -135,7 +233,7 @@ __global__ __launch_bounds__(kSmallThreads) void quant_dynamic_small_kernel(Quan
       if (u < T) {
         uint32_t r, c0;
         unit_coords(a, u, r, c0);
-        v[i] = unit_load(a, r, c0);
+        v[i] = src.load(a, r, c0);
       }
     }
 #pragma unroll
@@ -151,20 +249,23 @@ __global__ __launch_bounds__(kSmallThreads) void quant_dynamic_small_kernel(Quan
   if (u < T) {
     uint32_t r, c0;
     unit_coords(a, u, r, c0);
+    src.emit(a, r, c0, keep);
     unit_store(a, r, c0, keep, s);
   }
 }
 
 // Launch 1 of 2: per-block maxima of |x| (as bf16 magnitude bits).
-__global__ __launch_bounds__(256) void absmax_partial_kernel(QuantArgs a, uint32_t* partial) {
+template <class Src>
+__global__ __launch_bounds__(256) void absmax_partial_kernel(QuantArgs a, Src src, uint32_t* partial) {
   __shared__ uint32_t red[16];
-  uint32_t m = absmax_range(a, blockIdx.x * blockDim.x + threadIdx.x, a.total_units, gridDim.x * blockDim.x);
+  uint32_t m = absmax_range(a, src, blockIdx.x * blockDim.x + threadIdx.x, a.total_units, gridDim.x * blockDim.x);
   m = block_max_u32(m, red);
   if (threadIdx.x == 0) partial[blockIdx.x] = m;
 }
 
 // Launch 2 of 2: fold the maxima, derive the scale, quantize.
-__global__ __launch_bounds__(256) void quant_from_partial_kernel(QuantArgs a, const uint32_t* partial,
+template <class Src>
+__global__ __launch_bounds__(256) void quant_from_partial_kernel(QuantArgs a, Src src, const uint32_t* partial,
                                                                   uint32_t nparts, float* scale_out) {
   __shared__ uint32_t red[16];
   uint32_t m = 0;
@@ -172,24 +273,68 @@ __global__ __launch_bounds__(256) void quant_from_partial_kernel(QuantArgs a, co
   m = block_max_u32(m, red);
   const float s = scale_from_amax(bf16_to_f32(m));
   if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
-  quant_range(a, blockIdx.x * blockDim.x + threadIdx.x, a.total_units, gridDim.x * blockDim.x, s);
+  quant_range(a, src, blockIdx.x * blockDim.x + threadIdx.x, a.total_units, gridDim.x * blockDim.x, s);
 }
 
-__global__ __launch_bounds__(256) void quant_static_kernel(QuantArgs a, const float* scale) {
+__global__ __launch_bounds__(256) void quant_static_kernel(QuantArgs a, PlainSrc src, const float* scale) {
   const float s = *scale;
-  quant_range(a, blockIdx.x * blockDim.x + threadIdx.x, a.total_units, gridDim.x * blockDim.x, s);
+  quant_range(a, src, blockIdx.x * blockDim.x + threadIdx.x, a.total_units, gridDim.x * blockDim.x, s);
 }
 
 // One workgroup per row: the row's own amax and scale, then its codes.
-__global__ __launch_bounds__(256) void quant_per_row_kernel(QuantArgs a, float* scales_out) {
+__global__ __launch_bounds__(256) void quant_per_row_kernel(QuantArgs a, PlainSrc src, float* scales_out) {
   __shared__ uint32_t red[16];
   const uint32_t r = blockIdx.x;
   const uint32_t u0 = r * a.units_per_row, u1 = u0 + a.units_per_row;
-  uint32_t m = absmax_range(a, u0 + threadIdx.x, u1, blockDim.x);
+  uint32_t m = absmax_range(a, src, u0 + threadIdx.x, u1, blockDim.x);
   m = block_max_u32(m, red);
   const float s = scale_from_amax(bf16_to_f32(m));
   if (threadIdx.x == 0) scales_out[r] = s;
-  quant_range(a, u0 + threadIdx.x, u1, blockDim.x, s);
+  quant_range(a, src, u0 + threadIdx.x, u1, blockDim.x, s);
+}
+
+// Residual add and RMS statistics, one workgroup per row: h' = bf16(h + d)
+// (float32 add, one rounding; written to h_out when d is given), then
+// inv_rms[row] = 1 / sqrt(sum(h'^2) / cols + eps) in float32.  The sum runs
+// in a fixed order (per-thread units in order, then a fixed butterfly and
+// wave order), so it is deterministic.
+__global__ __launch_bounds__(256) void row_stats_kernel(const uint16_t* h, int64_t ld_h, const uint16_t* d,
+                                                        int64_t ld_d, uint16_t* h_out, int64_t ld_ho, uint32_t cols,
+                                                        uint32_t units_per_row, float eps, bool vec,
+                                                        float* inv_rms) {
+  __shared__ float wsum[4];
+  const uint32_t r = blockIdx.x;
+  const uint16_t* hrow = h + (int64_t)r * ld_h;
+  const uint16_t* drow = d ? d + (int64_t)r * ld_d : nullptr;
+  uint16_t* orow = d ? h_out + (int64_t)r * ld_ho : nullptr;
+  float acc = 0.0f;
+  for (uint32_t u = threadIdx.x; u < units_per_row; u += blockDim.x) {
+    const uint32_t c0 = u * 8;
+    v4i hv = load8_bf16(hrow, c0, cols, vec);
+    if (drow != nullptr) {
+      const v4i dv = load8_bf16(drow, c0, cols, vec);
+      float f[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[i] = bf16_at(hv, i) + bf16_at(dv, i);
+      hv = pack8_bf16(f);
+      store8_bf16(orow, c0, cols, vec, hv);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float x = bf16_at(hv, i);
+      acc = __builtin_fmaf(x, x, acc);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) wsum[wave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.0f;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += wsum[w];
+    inv_rms[r] = 1.0f / sqrtf(t / (float)cols + eps);
+  }
 }
 
 __global__ void write_scale_kernel(float* scale_out, float v) { *scale_out = v; }
@@ -199,20 +344,22 @@ __global__ void fill_scales_kernel(float* scales, uint32_t n, float v) {
   if (i < n) scales[i] = v;
 }
 
-QuantArgs make_args(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q) {
+QuantArgs make_args(int64_t rows, int64_t cols, uint8_t* q, int64_t ld_q) {
   QuantArgs a;
-  a.x = x;
   a.q = q;
-  a.ld_x = ld_x;
   a.ld_q = ld_q;
   a.rows = (uint32_t)rows;
   a.cols = (uint32_t)cols;
   a.units_per_row = (uint32_t)((cols + 7) / 8);
   a.total_units = a.rows * a.units_per_row;
   a.div_units = make_fastdiv(a.units_per_row);
-  a.vec = ((uintptr_t)x % 16 == 0) && (ld_x % 8 == 0) && ((uintptr_t)q % 8 == 0) && (ld_q % 8 == 0);
+  a.vec_q = ((uintptr_t)q % 8 == 0) && (ld_q % 8 == 0);
   return a;
 }
+
+bool rows16(const void* p, int64_t ld) { return ((uintptr_t)p % 16 == 0) && (ld % 8 == 0); }
+
+PlainSrc plain_src(const uint16_t* x, int64_t ld_x) { return PlainSrc{x, ld_x, rows16(x, ld_x)}; }
 
 constexpr uint32_t kPartialBlocks = 1024;         // max blocks of the two-launch path
 constexpr uint32_t kSmallUnits = 1u << 15;        // <= 256 Ki elements (512 KiB): one launch
@@ -222,39 +369,86 @@ uint32_t grid_for_units(uint32_t units, uint32_t per_block, uint32_t cap) {
   return g < 1 ? 1 : (g > cap ? cap : g);
 }
 
+// Dynamic per-tensor quantization of any source: one launch for small
+// tensors of cheap sources, else two (per-block maxima in the workspace).
+template <class Src>
+hipError_t launch_dynamic(const QuantArgs& a, const Src& src, bool small_ok, float* scale_out, void* workspace,
+                          hipStream_t stream) {
+  if (small_ok && a.total_units <= kSmallUnits) {
+    // one workgroup per 1024-unit slot: at most kSmallUnits / 1024 = 32
+    const uint32_t grid = (a.total_units + kSmallThreads - 1) / kSmallThreads;
+    quant_dynamic_small_kernel<Src><<<grid, kSmallThreads, 0, stream>>>(a, src, scale_out);
+    return hipGetLastError();
+  }
+  uint32_t* partial = static_cast<uint32_t*>(workspace);
+  const uint32_t grid = grid_for_units(a.total_units, 256 * kUnroll, kPartialBlocks);
+  absmax_partial_kernel<Src><<<grid, 256, 0, stream>>>(a, src, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const uint32_t grid2 = grid_for_units(a.total_units, 256 * kUnroll, 8192);
+  quant_from_partial_kernel<Src><<<grid2, 256, 0, stream>>>(a, src, partial, grid, scale_out);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t quant_workspace_bytes() { return kPartialBlocks * sizeof(uint32_t); }
 
-// Shapes were validated by the caller: 0 <= rows, cols; rows*cols/8 < 2^32.
+// Shapes were validated by the caller: 0 <= rows, cols; rows*cols/8 < 2^31.
 hipError_t launch_quant_dynamic(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
                                 int64_t ld_q, float* scale_out, void* workspace, hipStream_t stream) {
   if (rows == 0 || cols == 0) {
     write_scale_kernel<<<1, 1, 0, stream>>>(scale_out, 1.0f);
     return hipGetLastError();
   }
-  QuantArgs a = make_args(x, rows, cols, ld_x, q, ld_q);
-  if (a.total_units <= kSmallUnits) {
-    // one workgroup per 1024-unit slot: at most kSmallUnits / 1024 = 32
-    const uint32_t grid = (a.total_units + kSmallThreads - 1) / kSmallThreads;
-    quant_dynamic_small_kernel<<<grid, kSmallThreads, 0, stream>>>(a, scale_out);
+  return launch_dynamic(make_args(rows, cols, q, ld_q), plain_src(x, ld_x), true, scale_out, workspace, stream);
+}
+
+size_t norm_quant_workspace_bytes(int64_t rows) {
+  return quant_workspace_bytes() + (size_t)((rows * 4 + 255) / 256 * 256);
+}
+
+hipError_t launch_add_rmsnorm_quant(const uint16_t* h, int64_t ld_h, const uint16_t* delta, int64_t ld_delta,
+                                    uint16_t* h_out, int64_t ld_h_out, int64_t rows, int64_t cols, float eps,
+                                    uint16_t* y_out, int64_t ld_y, uint8_t* q, int64_t ld_q, float* scale_out,
+                                    void* workspace, hipStream_t stream) {
+  if (rows == 0 || cols == 0) {
+    write_scale_kernel<<<1, 1, 0, stream>>>(scale_out, 1.0f);
     return hipGetLastError();
   }
-  uint32_t* partial = static_cast<uint32_t*>(workspace);
-  const uint32_t grid = grid_for_units(a.total_units, 256 * kUnroll, kPartialBlocks);
-  absmax_partial_kernel<<<grid, 256, 0, stream>>>(a, partial);
+  float* inv_rms = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + quant_workspace_bytes());
+  const bool vec = rows16(h, ld_h) && (delta == nullptr || (rows16(delta, ld_delta) && rows16(h_out, ld_h_out)));
+  const QuantArgs a = make_args(rows, cols, q, ld_q);
+  row_stats_kernel<<<(uint32_t)rows, 256, 0, stream>>>(h, ld_h, delta, ld_delta, h_out, ld_h_out, (uint32_t)cols,
+                                                        a.units_per_row, eps, vec, inv_rms);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const uint32_t grid2 = grid_for_units(a.total_units, 256 * kUnroll, 8192);
-  quant_from_partial_kernel<<<grid2, 256, 0, stream>>>(a, partial, grid, scale_out);
-  return hipGetLastError();
+  const uint16_t* hs = delta ? h_out : h;
+  const int64_t ld_hs = delta ? ld_h_out : ld_h;
+  const NormSrc src{hs, ld_hs, inv_rms, y_out, ld_y, rows16(hs, ld_hs), y_out != nullptr && rows16(y_out, ld_y)};
+  return launch_dynamic(a, src, true, scale_out, workspace, stream);
+}
+
+hipError_t launch_silu_mul_quant(const uint16_t* gu, int64_t ld_gu, int64_t rows, int64_t cols, uint16_t* y_out,
+                                 int64_t ld_y, uint8_t* q, int64_t ld_q, float* scale_out, void* workspace,
+                                 hipStream_t stream) {
+  if (rows == 0 || cols == 0) {
+    write_scale_kernel<<<1, 1, 0, stream>>>(scale_out, 1.0f);
+    return hipGetLastError();
+  }
+  // the up half starts at column cols: aligned only if cols % 8 == 0
+  const SiluMulSrc src{gu, ld_gu, y_out, ld_y, rows16(gu, ld_gu) && (cols % 8 == 0),
+                       y_out != nullptr && rows16(y_out, ld_y)};
+  // the activation is costly to evaluate: never the redundant one-launch path
+  return launch_dynamic(make_args(rows, cols, q, ld_q), src, false, scale_out, workspace, stream);
 }
 
 hipError_t launch_quant_static(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, const float* scale,
                                uint8_t* q, int64_t ld_q, hipStream_t stream) {
   if (rows == 0 || cols == 0) return hipSuccess;
-  QuantArgs a = make_args(x, rows, cols, ld_x, q, ld_q);
-  quant_static_kernel<<<grid_for_units(a.total_units, 256 * kUnroll, 8192), 256, 0, stream>>>(a, scale);
+  QuantArgs a = make_args(rows, cols, q, ld_q);
+  quant_static_kernel<<<grid_for_units(a.total_units, 256 * kUnroll, 8192), 256, 0, stream>>>(a, plain_src(x, ld_x),
+                                                                                               scale);
   return hipGetLastError();
 }
 
@@ -265,8 +459,8 @@ hipError_t launch_quant_per_row(const uint16_t* x, int64_t rows, int64_t cols, i
     fill_scales_kernel<<<(uint32_t)((rows + 255) / 256), 256, 0, stream>>>(scales_out, (uint32_t)rows, 1.0f);
     return hipGetLastError();
   }
-  QuantArgs a = make_args(x, rows, cols, ld_x, q, ld_q);
-  quant_per_row_kernel<<<(uint32_t)rows, 256, 0, stream>>>(a, scales_out);
+  QuantArgs a = make_args(rows, cols, q, ld_q);
+  quant_per_row_kernel<<<(uint32_t)rows, 256, 0, stream>>>(a, plain_src(x, ld_x), scales_out);
   return hipGetLastError();
 }
 

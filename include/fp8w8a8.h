@@ -157,9 +157,11 @@ fp8_status fp8_quant_dynamic_per_row(const uint16_t* x_bf16, int64_t rows, int64
  *   accum  FP8_ACCUM_FP32 or FP8_ACCUM_FP8_MFMA
  *   bias   N bf16 values, or NULL for none
  *   out    [M, N] bf16, row pitch ldo >= N            (output)
- * M <= 16 runs the skinny (decode) kernel, which streams the weight once
- * with no padding or repacking; larger M runs the LDS-staged matrix-core
- * GEMM.  Any M, N, K >= 1 is accepted.
+ * M <= 64 runs the skinny (decode) kernel, one 16-row block of M per grid
+ * row, which streams the weight once with no padding or repacking; larger M
+ * runs the LDS-staged matrix-core GEMM (and layouts it does not take -- rows
+ * not 16-byte aligned or K % 16 != 0 -- the skinny kernel).  Any M, N,
+ * K >= 1 is accepted.
  * Errors: INVALID_ARG for null pointers (bias may be NULL), negative M or
  * N, K < 1, lda/ldw < K, ldo < N, or an unknown scale or accumulation mode.
  */
@@ -167,6 +169,64 @@ fp8_status fp8_scaled_mm(const uint8_t* a_q, int64_t lda, const uint8_t* w_q, in
                          const float* s_a, const float* s_w, fp8_scale_mode mode,
                          fp8_accum_mode accum, const uint16_t* bias_bf16, uint16_t* out_bf16,
                          int64_t ldo, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * Producer-fused quantization: the step that feeds a linear, computed and
+ * quantized in the same pass, so its bf16 result never travels through
+ * memory.  The review of "[WIP] FP8 support" (text-generation-inference PR
+ * 1484) asks to remove the unnecessary operations around the FP8 GEMM; the
+ * pages do not define the producers themselves, so their definitions are
+ * readings: a Llama-shaped block's residual add, unit-weight RMS
+ * normalization, and gate-first SiLU*mul, each rounded once to bf16.
+ * The quantization is exactly fp8_quant_dynamic's, applied to those bf16
+ * values.  Workspace contents are scratch between the kernels of one call.
+ */
+
+/* Bytes of workspace fp8_add_rmsnorm_quant_dynamic needs for `rows` rows. */
+size_t fp8_norm_quant_workspace_bytes(int64_t rows);
+
+/*
+ * h' = bf16(h + delta)             (float32 add, one rounding; skipped when
+ *                                   delta is NULL: h' = h)
+ * y  = bf16(h' / sqrt(mean_c(h'^2) + eps))   per row, float32 math
+ * (q, *scale_out) = dynamic per-tensor quantization of y
+ *
+ *   h_bf16     [rows, cols], pitch ld_h                 (residual stream in)
+ *   delta_bf16 [rows, cols], pitch ld_delta, or NULL    (added first)
+ *   h_out_bf16 [rows, cols], pitch ld_h_out: receives h' (required iff
+ *              delta is given; must not overlap h or delta)
+ *   eps        finite, >= 0 (1e-5 for Llama-shaped blocks)
+ *   y_out_bf16 [rows, cols], pitch ld_y, or NULL: receives y, the exact
+ *              values that were quantized
+ *   q_e4m3, ld_q, scale_out  as fp8_quant_dynamic
+ *   workspace  fp8_norm_quant_workspace_bytes(rows) bytes
+ * Errors: as fp8_quant_dynamic, plus INVALID_ARG for a missing h_out when
+ * delta is given, pitches smaller than cols, or a negative/non-finite eps.
+ */
+fp8_status fp8_add_rmsnorm_quant_dynamic(const uint16_t* h_bf16, int64_t ld_h,
+                                         const uint16_t* delta_bf16, int64_t ld_delta,
+                                         uint16_t* h_out_bf16, int64_t ld_h_out,
+                                         int64_t rows, int64_t cols, float eps,
+                                         uint16_t* y_out_bf16, int64_t ld_y,
+                                         uint8_t* q_e4m3, int64_t ld_q, float* scale_out,
+                                         void* workspace, void* stream);
+
+/*
+ * m = bf16(silu(g) * u), silu(g) = g / (1 + exp(-g)) in float32, where row r
+ * of gu_bf16 holds the gate in columns [0, cols) and the up projection in
+ * [cols, 2 cols) (a fused gate_up linear's output);
+ * (q, *scale_out) = dynamic per-tensor quantization of m.
+ *
+ *   gu_bf16   [rows, 2 cols], pitch ld_gu >= 2 cols     (input)
+ *   y_out_bf16 [rows, cols], pitch ld_y, or NULL: receives m
+ *   q_e4m3    [rows, cols], pitch ld_q; scale_out as fp8_quant_dynamic
+ *   workspace fp8_quant_workspace_bytes() bytes
+ * Errors: as fp8_quant_dynamic, plus INVALID_ARG for ld_gu < 2 cols.
+ */
+fp8_status fp8_silu_mul_quant_dynamic(const uint16_t* gu_bf16, int64_t ld_gu, int64_t rows,
+                                      int64_t cols, uint16_t* y_out_bf16, int64_t ld_y,
+                                      uint8_t* q_e4m3, int64_t ld_q, float* scale_out,
+                                      void* workspace, void* stream);
 
 /* Text describing the calling thread's most recent non-OK status. */
 const char* fp8_last_error(void);

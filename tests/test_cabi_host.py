@@ -32,7 +32,8 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "fp8_quant_workspace_bytes", "fp8_quant_dynamic", "fp8_quant_static",
-        "fp8_quant_dynamic_per_row", "fp8_scaled_mm", "fp8_last_error"])
+        "fp8_quant_dynamic_per_row", "fp8_scaled_mm", "fp8_last_error",
+        "fp8_norm_quant_workspace_bytes", "fp8_add_rmsnorm_quant_dynamic", "fp8_silu_mul_quant_dynamic"])
 
 
 def test_library_exports_every_declared_function(lib):
@@ -98,3 +99,25 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fp8, "_lib", None)
     with pytest.raises(fp8.Fp8Error, match="no fallback"):
         fp8.lib()
+
+
+def test_fused_producers_reject_bad_arguments(lib):
+    F = ctypes.c_float
+    f = lib.fp8_add_rmsnorm_quant_dynamic
+    # h, ld_h, delta, ld_delta, h_out, ld_h_out, rows, cols, eps, y, ld_y, q, ld_q, scale, ws, stream
+    assert f(P, 8, P, 8, NULL, 0, 2, 8, F(1e-5), NULL, 0, P, 8, P, P, NULL) == INVALID        # delta without h_out
+    assert "h_out" in _err(lib)
+    assert f(P, 8, P, 4, P, 8, 2, 8, F(1e-5), NULL, 0, P, 8, P, P, NULL) == INVALID           # ld_delta < cols
+    assert f(P, 8, NULL, 0, NULL, 0, 2, 8, F(-1.0), NULL, 0, P, 8, P, P, NULL) == INVALID     # eps < 0
+    assert f(P, 8, NULL, 0, NULL, 0, 2, 8, F(float("nan")), NULL, 0, P, 8, P, P, NULL) == INVALID
+    assert f(P, 8, NULL, 0, NULL, 0, 2, 8, F(1e-5), P, 4, P, 8, P, P, NULL) == INVALID        # ld_y < cols
+    assert f(P, 8, NULL, 0, NULL, 0, 2, 8, F(1e-5), NULL, 0, P, 8, NULL, P, NULL) == INVALID  # null scale
+    assert f(P, 8, NULL, 0, NULL, 0, 2, 8, F(1e-5), NULL, 0, P, 8, P, NULL, NULL) == INVALID  # null workspace
+    g = lib.fp8_silu_mul_quant_dynamic
+    # gu, ld_gu, rows, cols, y, ld_y, q, ld_q, scale, ws, stream
+    assert g(P, 12, 2, 8, NULL, 0, P, 8, P, P, NULL) == INVALID     # ld_gu < 2 cols
+    assert "2 * cols" in _err(lib)
+    assert g(P, 16, 2, 8, NULL, 0, P, 8, NULL, P, NULL) == INVALID  # null scale
+    assert g(P, 16, 2, 8, NULL, 0, P, 8, P, NULL, NULL) == INVALID  # null workspace
+    assert g(P, 16, -2, 8, NULL, 0, P, 8, P, P, NULL) == INVALID
+    assert lib.fp8_norm_quant_workspace_bytes(16384) >= lib.fp8_quant_workspace_bytes() + 4 * 16384

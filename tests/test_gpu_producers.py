@@ -1,0 +1,94 @@
+"""Producer-fused quantization on the GPU vs the CPU oracle.
+
+The residual add is bit-exact.  The normalized / activated bf16 values come
+from float32 math on the GPU and float64 math in the oracle, so they agree to
+within one bf16 step (almost always exactly).  The quantization is checked
+teacher-forced: the codes and the scale must equal the oracle's dynamic
+quantization of the very bf16 values the GPU wrote out, bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp8_w8a8_quantized_amd as fp8
+from fp8_w8a8_quantized_amd import synth
+from _helpers import say, dev_bf16, host_u8, host_f32, host_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _pitched(bits, pitch):
+    """A device bf16 view [rows, cols] inside a wider [rows, pitch] buffer."""
+    rows, cols = bits.shape
+    buf = np.zeros((rows, pitch), np.uint16)
+    buf[:, :cols] = bits
+    return dev_bf16(buf)[:, :cols]
+
+
+def _check_quant_of(y_bits, q, s):
+    q_ref, s_ref = oracle.quant_dynamic(y_bits)
+    assert host_f32(s)[0] == np.float32(s_ref)
+    assert np.array_equal(host_u8(q), q_ref)
+
+
+@pytest.mark.parametrize("rows,cols,pitch,with_delta", [
+    (16, 4096, 4096, True),      # decode, one-launch quantization
+    (16, 4096, 4096, False),
+    (300, 4096, 4096, True),     # two-launch quantization
+    (5, 1003, 1011, True),       # ragged row ends, odd pitch
+    (1, 14336, 14336, True),
+])
+def test_add_rmsnorm_quant(rows, cols, pitch, with_delta):
+    say("add_rmsnorm_quant", rows, cols, pitch, with_delta)
+    h = synth.activations(41, rows, cols, outliers=True)
+    d = synth.activations(42, rows, cols, outliers=False)
+    hd = _pitched(h, pitch)
+    dd = _pitched(d, pitch) if with_delta else None
+    h_out = _pitched(np.zeros_like(h), pitch) if with_delta else None
+    y = torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")
+    q, s, h2, _ = fp8.add_rmsnorm_quant(hd, dd, h_out=h_out, y_out=y)
+    torch.cuda.synchronize()
+    if with_delta:
+        h_ref = oracle.add_bf16(h, d)
+        assert np.array_equal(host_bf16_bits(h2), h_ref)
+    else:
+        h_ref = h
+    y_gpu = host_bf16_bits(y)
+    dist = oracle.bf16_ulp_distance(y_gpu, oracle.rmsnorm(h_ref, 1e-5))
+    assert dist.max() <= 1 and np.mean(dist == 0) >= 0.99, (dist.max(), np.mean(dist == 0))
+    _check_quant_of(y_gpu, q, s)
+    # the optional copy does not change the codes
+    q2, s2, _, _ = fp8.add_rmsnorm_quant(hd, dd, h_out=torch.empty_like(hd) if with_delta else None)
+    torch.cuda.synchronize()
+    assert torch.equal(q2, q) and torch.equal(s2, s)
+
+
+@pytest.mark.parametrize("rows,cols,pitch", [
+    (16, 14336, 2 * 14336),      # decode gate_up output
+    (64, 14336, 2 * 14336),
+    (3, 1001, 2 * 1001 + 5),     # ragged, odd pitch (unaligned up half)
+])
+def test_silu_mul_quant(rows, cols, pitch):
+    say("silu_mul_quant", rows, cols, pitch)
+    gu = synth.activations(43, rows, 2 * cols, outliers=True)
+    gud = _pitched(gu, pitch)
+    y = torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")
+    q, s, _ = fp8.silu_mul_quant(gud, y_out=y)
+    torch.cuda.synchronize()
+    y_gpu = host_bf16_bits(y)
+    dist = oracle.bf16_ulp_distance(y_gpu, oracle.silu_mul(gu, cols))
+    assert dist.max() <= 1 and np.mean(dist == 0) >= 0.99, (dist.max(), np.mean(dist == 0))
+    _check_quant_of(y_gpu, q, s)
+    q2, s2, _ = fp8.silu_mul_quant(gud)
+    torch.cuda.synchronize()
+    assert torch.equal(q2, q) and torch.equal(s2, s)
+
+
+def test_producers_empty():
+    h = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    q, s, _, _ = fp8.add_rmsnorm_quant(h)
+    gu = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    q2, s2, _ = fp8.silu_mul_quant(gu)
+    torch.cuda.synchronize()
+    assert host_f32(s)[0] == 1.0 and host_f32(s2)[0] == 1.0
