@@ -92,6 +92,26 @@ __device__ __forceinline__ float bf16_at(v4i v, int i) {
   return bf16_to_f32((i & 1) ? (w >> 16) : (w & 0xffffu));
 }
 
+// float64 -> bf16 bits, one round-to-nearest-even (no double rounding through
+// float32): the value is rounded to a multiple of its bf16 step 2^max(e-8,
+// -133), where 2^(e-1) <= |x| < 2^e; the result is a bf16 value, exact in
+// float32.  Finite inputs (NaN stays NaN).
+__device__ __forceinline__ uint32_t f64_to_bf16_rne(double x) {
+  if (x != x) return 0x7fc0u;
+  int e;
+  (void)frexp(x, &e);
+  const double step = ldexp(1.0, max(e - 8, -133));
+  const double r = rint(x / step) * step;
+  return __float_as_uint((float)r) >> 16;
+}
+
+__device__ __forceinline__ v4i pack8_bf16_f64(const double f[8]) {
+  v4i v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = (int)(f64_to_bf16_rne(f[2 * i]) | (f64_to_bf16_rne(f[2 * i + 1]) << 16));
+  return v;
+}
+
 __device__ __forceinline__ v4i pack8_bf16(const float f[8]) {
   v4i v;
 #pragma unroll
@@ -115,22 +135,22 @@ struct PlainSrc {
   __device__ __forceinline__ void emit(const QuantArgs&, uint32_t, uint32_t, v4i) const {}
 };
 
-// Unit-weight RMS normalization: y = bf16(h * inv_rms[row]), inv_rms from
-// row_stats_kernel.
+// Unit-weight RMS normalization: y = bf16(h * inv_rms[row]) in float64,
+// inv_rms from row_stats_kernel.
 struct NormSrc {
   const uint16_t* h;
   int64_t ld_h;
-  const float* inv_rms;
+  const double* inv_rms;
   uint16_t* y;  // optional copy of the normalized values
   int64_t ld_y;
   bool vec_h, vec_y;
   __device__ __forceinline__ v4i load(const QuantArgs& a, uint32_t r, uint32_t c0) const {
     const v4i hv = load8_bf16(h + (int64_t)r * ld_h, c0, a.cols, vec_h);
-    const float g = inv_rms[r];
-    float f[8];
+    const double g = inv_rms[r];
+    double f[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = bf16_at(hv, i) * g;
-    return pack8_bf16(f);
+    for (int i = 0; i < 8; ++i) f[i] = (double)bf16_at(hv, i) * g;
+    return pack8_bf16_f64(f);
   }
   __device__ __forceinline__ void emit(const QuantArgs& a, uint32_t r, uint32_t c0, v4i v) const {
     if (y != nullptr) store8_bf16(y + (int64_t)r * ld_y, c0, a.cols, vec_y, v);
@@ -138,7 +158,7 @@ struct NormSrc {
 };
 
 // Gated activation, gate half first: y = bf16(silu(g) * u) with
-// silu(g) = g / (1 + exp(-g)) in float32.
+// silu(g) = g / (1 + exp(-g)), in float64.
 struct SiluMulSrc {
   const uint16_t* gu;  // row r: gate columns [0, cols), up columns [cols, 2 cols)
   int64_t ld;
@@ -149,13 +169,13 @@ struct SiluMulSrc {
     const uint16_t* row = gu + (int64_t)r * ld;
     const v4i gv = load8_bf16(row, c0, a.cols, vec);
     const v4i uv = load8_bf16(row + a.cols, c0, a.cols, vec);
-    float f[8];
+    double f[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float g = bf16_at(gv, i);
-      f[i] = g / (1.0f + expf(-g)) * bf16_at(uv, i);
+      const double g = bf16_at(gv, i);
+      f[i] = g / (1.0 + exp(-g)) * (double)bf16_at(uv, i);
     }
-    return pack8_bf16(f);
+    return pack8_bf16_f64(f);
   }
   __device__ __forceinline__ void emit(const QuantArgs& a, uint32_t r, uint32_t c0, v4i v) const {
     if (y != nullptr) store8_bf16(y + (int64_t)r * ld_y, c0, a.cols, vec_y, v);
@@ -295,19 +315,19 @@ __global__ __launch_bounds__(256) void quant_per_row_kernel(QuantArgs a, PlainSr
 
 // Residual add and RMS statistics, one workgroup per row: h' = bf16(h + d)
 // (float32 add, one rounding; written to h_out when d is given), then
-// inv_rms[row] = 1 / sqrt(sum(h'^2) / cols + eps) in float32.  The sum runs
+// inv_rms[row] = 1 / sqrt(sum(h'^2) / cols + eps) in float64.  The sum runs
 // in a fixed order (per-thread units in order, then a fixed butterfly and
 // wave order), so it is deterministic.
 __global__ __launch_bounds__(256) void row_stats_kernel(const uint16_t* h, int64_t ld_h, const uint16_t* d,
                                                         int64_t ld_d, uint16_t* h_out, int64_t ld_ho, uint32_t cols,
-                                                        uint32_t units_per_row, float eps, bool vec,
-                                                        float* inv_rms) {
-  __shared__ float wsum[4];
+                                                        uint32_t units_per_row, double eps, bool vec,
+                                                        double* inv_rms) {
+  __shared__ double wsum[4];
   const uint32_t r = blockIdx.x;
   const uint16_t* hrow = h + (int64_t)r * ld_h;
   const uint16_t* drow = d ? d + (int64_t)r * ld_d : nullptr;
   uint16_t* orow = d ? h_out + (int64_t)r * ld_ho : nullptr;
-  float acc = 0.0f;
+  double acc = 0.0;
   for (uint32_t u = threadIdx.x; u < units_per_row; u += blockDim.x) {
     const uint32_t c0 = u * 8;
     v4i hv = load8_bf16(hrow, c0, cols, vec);
@@ -321,8 +341,8 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const uint16_t* h, int64
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float x = bf16_at(hv, i);
-      acc = __builtin_fmaf(x, x, acc);
+      const double x = bf16_at(hv, i);
+      acc = __builtin_fma(x, x, acc);
     }
   }
 #pragma unroll
@@ -331,9 +351,9 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const uint16_t* h, int64
   if (lane == 0) wsum[wave] = acc;
   __syncthreads();
   if (threadIdx.x == 0) {
-    float t = 0.0f;
+    double t = 0.0;
     for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += wsum[w];
-    inv_rms[r] = 1.0f / sqrtf(t / (float)cols + eps);
+    inv_rms[r] = 1.0 / sqrt(t / (double)cols + eps);
   }
 }
 
@@ -405,7 +425,7 @@ hipError_t launch_quant_dynamic(const uint16_t* x, int64_t rows, int64_t cols, i
 }
 
 size_t norm_quant_workspace_bytes(int64_t rows) {
-  return quant_workspace_bytes() + (size_t)((rows * 4 + 255) / 256 * 256);
+  return quant_workspace_bytes() + (size_t)((rows * 8 + 255) / 256 * 256);
 }
 
 hipError_t launch_add_rmsnorm_quant(const uint16_t* h, int64_t ld_h, const uint16_t* delta, int64_t ld_delta,
@@ -416,11 +436,11 @@ hipError_t launch_add_rmsnorm_quant(const uint16_t* h, int64_t ld_h, const uint1
     write_scale_kernel<<<1, 1, 0, stream>>>(scale_out, 1.0f);
     return hipGetLastError();
   }
-  float* inv_rms = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + quant_workspace_bytes());
+  double* inv_rms = reinterpret_cast<double*>(static_cast<uint8_t*>(workspace) + quant_workspace_bytes());
   const bool vec = rows16(h, ld_h) && (delta == nullptr || (rows16(delta, ld_delta) && rows16(h_out, ld_h_out)));
   const QuantArgs a = make_args(rows, cols, q, ld_q);
   row_stats_kernel<<<(uint32_t)rows, 256, 0, stream>>>(h, ld_h, delta, ld_delta, h_out, ld_h_out, (uint32_t)cols,
-                                                        a.units_per_row, eps, vec, inv_rms);
+                                                        a.units_per_row, (double)eps, vec, inv_rms);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint16_t* hs = delta ? h_out : h;

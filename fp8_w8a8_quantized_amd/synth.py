@@ -70,6 +70,23 @@ def weights(config, n, k, layer=0, sub=0, row_multipliers=False, std=0.02):
     return f32_to_bf16_bits(w)
 
 
+def weights_device(config, n, k, layer=0, sub=0, row_multipliers=False, std=0.02, device="cuda"):
+    """torch.bfloat16 [n, k] on `device`, the weights recipe drawn by torch's
+    device generator (Philox) seeded from SeedSequence([config, layer, role,
+    sub]): for stacks of many large layers, whose host draws would dominate
+    set-up time.  The row multipliers come from the host generator above.
+    Copy the result to the host to hand the same values to the oracle."""
+    seed = int(np.random.SeedSequence([config, layer, ROLE_W, sub]).generate_state(1)[0])
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    w = torch.randn((n, k), generator=g, device=device, dtype=torch.float32)
+    w *= std
+    if row_multipliers:
+        u = generator(config, layer, ROLE_C, sub).uniform(np.log(0.25), np.log(4.0), size=n)
+        w *= torch.from_numpy(np.exp(u).astype(np.float32)).to(device)[:, None]
+    return w.to(torch.bfloat16)
+
+
 def bias(config, n, layer=0, sub=0, std=0.1):
     b = generator(config, layer, ROLE_BIAS, sub).standard_normal(n, dtype=np.float32)
     return f32_to_bf16_bits(b * np.float32(std))

@@ -120,4 +120,4 @@ def test_fused_producers_reject_bad_arguments(lib):
     assert g(P, 16, 2, 8, NULL, 0, P, 8, NULL, P, NULL) == INVALID  # null scale
     assert g(P, 16, 2, 8, NULL, 0, P, 8, P, NULL, NULL) == INVALID  # null workspace
     assert g(P, 16, -2, 8, NULL, 0, P, 8, P, P, NULL) == INVALID
-    assert lib.fp8_norm_quant_workspace_bytes(16384) >= lib.fp8_quant_workspace_bytes() + 4 * 16384
+    assert lib.fp8_norm_quant_workspace_bytes(16384) >= lib.fp8_quant_workspace_bytes() + 8 * 16384
