@@ -143,12 +143,88 @@ def cpu_baseline(m, lin_shapes, row_frac=8, budget_s=10.0):
     return done_bytes, done_flops, timed, threads, desc
 
 
+def run_chain(args):
+    """The chained-linears workload: prefill of 16 prompts x 1024 tokens
+    through the 32-layer stack, then decode steps at M = 16 whose input is the
+    previous step's output (the first: each prompt's last position).  Decode
+    steps replay one captured HIP graph; a few eager steps are timed too."""
+    from fp8_w8a8_quantized_amd import chain
+    steps = args.steps if args.steps is not None else 512
+    warmup = args.warmup if args.warmup is not None else 2
+    torch.cuda.set_device(0)
+    log("building the 32-layer stack")
+    c = chain.Chain(layers=32, accum=args.accum)
+    prompts, seq = 16, 1024
+    x = synth.bf16_bits_to_torch(synth.activations(5, prompts * seq, chain.D_MODEL, layer=100, outliers=True)).cuda()
+    c.forward(x)                                            # allocate prefill buffers, warm up
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    h = c.forward(x)
+    e1.record()
+    torch.cuda.synchronize()
+    prefill_ms = e0.elapsed_time(e1)
+    start = h[seq - 1::seq].contiguous()
+    xin, xout = start.clone(), torch.empty_like(start)
+    for _ in range(warmup):
+        c.forward(xin, out=xout)
+    torch.cuda.synchronize()
+    # eager decode steps (Python launches every kernel)
+    n_eager = 8
+    xin.copy_(start)
+    e0.record()
+    for _ in range(n_eager):
+        c.forward(xin, out=xout)
+        xin.copy_(xout)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / n_eager
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        c.forward(xin, out=xout)
+        xin.copy_(xout)
+    xin.copy_(start)
+    g.replay()
+    torch.cuda.synchronize()
+    xin.copy_(start)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    decode_ms = (time.perf_counter() - t0) * 1e3 / steps
+    weight_bytes = 32 * sum(k * n for (_, k, n) in chain.SHAPES)
+    prefill_flops = 32 * sum(2 * prompts * seq * k * n for (_, k, n) in chain.SHAPES)
+    line = {
+        "metric": METRIC + " -- chained-linears workload", "value": round(weight_bytes / (decode_ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(decode_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8e4m3 in, bf16 out; " + ("fp8 matrix-core sums (prefill)" if args.accum == "fp8"
+                                            else "fp32-class sums (bf16 matrix cores on exact e4m3 values)"),
+        "data": "synthetic",
+        "config": {"workload": "32-layer Llama-3-8B-shaped stack of W8A8 linears (qkv, o, gate_up, down per layer, "
+                               "channelwise weights, fresh dynamic activation scale before every linear; RMSNorm, "
+                               "SiLU*mul and residual adds between them): 16 x 1024-token prefill, then decode "
+                               "steps at M=16 fed by the previous step",
+                   "layers": 32, "prefill_tokens": prompts * seq, "decode_M": prompts,
+                   "launch": "decode: hip_graph per step; prefill: eager"},
+        "chain": {"prefill_ms": round(prefill_ms, 2),
+                  "prefill_tflops": round(prefill_flops / (prefill_ms * 1e-3) / 1e12, 1),
+                  "decode_ms_per_step_graph": round(decode_ms, 4), "decode_ms_per_step_eager": round(eager_ms, 4),
+                  "decode_total_s": round(decode_ms * steps / 1e3, 3),
+                  "weight_bytes_per_decode_step": weight_bytes},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", choices=["decode", "prefill"], default="decode")
+    ap.add_argument("--workload", choices=["decode", "prefill", "chain"], default="decode",
+                    help="chain: the 32-layer Llama-3-8B-shaped stack, 16 x 1024-token prefill, then decode steps "
+                         "at M=16 (--steps of them, default 512)")
     ap.add_argument("--accum", choices=["fp32", "fp8"], default="fp32",
                     help="GEMM accumulation: fp32-class sums (default) or the fp8 matrix cores (M > 16)")
     ap.add_argument("--eager", action="store_true",
@@ -162,6 +238,8 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the layer would shard column-parallel over N; see the design notes).", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "chain":
+        return run_chain(args)
     decode = args.workload == "decode"
     m = 16 if decode else 16384
     steps = args.steps if args.steps is not None else (200 if decode else 20)
