@@ -188,7 +188,8 @@ size_t fp8_norm_quant_workspace_bytes(int64_t rows);
 /*
  * h' = bf16(h + delta)             (float32 add, one rounding; skipped when
  *                                   delta is NULL: h' = h)
- * y  = bf16(h' / sqrt(mean_c(h'^2) + eps))   per row, float32 math
+ * y  = bf16(h' / sqrt(mean_c(h'^2) + eps))   per row, float64 math, one
+ *                                             rounding to bf16
  * (q, *scale_out) = dynamic per-tensor quantization of y
  *
  *   h_bf16     [rows, cols], pitch ld_h                 (residual stream in)
@@ -212,7 +213,7 @@ fp8_status fp8_add_rmsnorm_quant_dynamic(const uint16_t* h_bf16, int64_t ld_h,
                                          void* workspace, void* stream);
 
 /*
- * m = bf16(silu(g) * u), silu(g) = g / (1 + exp(-g)) in float32, where row r
+ * m = bf16(silu(g) * u), silu(g) = g / (1 + exp(-g)) in float64, where row r
  * of gu_bf16 holds the gate in columns [0, cols) and the up projection in
  * [cols, 2 cols) (a fused gate_up linear's output);
  * (q, *scale_out) = dynamic per-tensor quantization of m.
