@@ -29,6 +29,8 @@ need checkpoints and datasets that are not available: parity unpinned for
 those, and for any multi-layer drift.
 """
 from .e4m3 import E4M3_MAX, decode, encode, positive_grid  # noqa: F401
+from . import e5m2  # noqa: F401
+from .w8a8 import FORMATS  # noqa: F401
 from .w8a8 import (  # noqa: F401
     bf16_bits_to_f32,
     amax,

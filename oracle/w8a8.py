@@ -26,9 +26,15 @@ always), and the epilogue is fp64 and left unrounded.
 """
 import numpy as np
 
+from . import e4m3, e5m2
 from .e4m3 import E4M3_MAX, decode, encode
 
 _F32_MAX = np.float32(E4M3_MAX)
+
+# The two fp8 formats: (decode, encode, largest finite value).  e4m3 is the
+# pages' format; e5m2 is the extension "Fp8 Quantization Support" names.
+FORMATS = {"e4m3": (e4m3.decode, e4m3.encode, np.float32(e4m3.E4M3_MAX)),
+           "e5m2": (e5m2.decode, e5m2.encode, np.float32(e5m2.E5M2_MAX))}
 
 
 def bf16_bits_to_f32(bits):
@@ -45,39 +51,40 @@ def amax(x_f32):
     return np.float32(np.max(np.abs(x_f32)))
 
 
-def scale_from_amax(a):
-    """Per-tensor scale mapping amax onto the e4m3fn maximum 448.
+def scale_from_amax(a, fmt="e4m3"):
+    """Per-tensor scale mapping amax onto the format's largest value.
 
-    s = fl32(amax / 448) (one correctly rounded float32 division); an
-    all-zero (or empty) tensor has no range to map and takes s = 1.
+    s = fl32(amax / max) (one correctly rounded float32 division; max = 448
+    for e4m3, 57344 for e5m2); an all-zero (or empty) tensor has no range to
+    map and takes s = 1.
     """
     a = np.float32(a)
     if a == 0:
         return np.float32(1.0)
-    return np.float32(a / _F32_MAX)
+    return np.float32(a / FORMATS[fmt][2])
 
 
-def quant_static(x_bits, scale):
+def quant_static(x_bits, scale, fmt="e4m3"):
     """Quantize bf16 bits with a given float32 scale: enc(fl32(x / scale)).
 
     The division is float32 and correctly rounded, then the saturating RNE
-    encoder runs on that float32 quotient.
+    encoder of the format runs on that float32 quotient.
     """
     x = bf16_bits_to_f32(x_bits)
     s = np.float32(scale)
     with np.errstate(over="ignore", divide="ignore", invalid="ignore"):
         v = (x / s).astype(np.float32)
-    return encode(v)
+    return FORMATS[fmt][1](v)
 
 
-def quant_dynamic(x_bits):
+def quant_dynamic(x_bits, fmt="e4m3"):
     """Dynamic per-tensor activation quantization: returns (codes, scale)."""
     x = bf16_bits_to_f32(x_bits)
-    s = scale_from_amax(amax(x))
-    return quant_static(x_bits, s), s
+    s = scale_from_amax(amax(x), fmt)
+    return quant_static(x_bits, s, fmt), s
 
 
-def quant_weight(w_bits, per_channel):
+def quant_weight(w_bits, per_channel, fmt="e4m3"):
     """Weight quantization, [N, K] bf16 bits -> (codes [N, K], scales).
 
     Per tensor: one scale from the amax of the whole matrix (shape [1]).
@@ -86,33 +93,37 @@ def quant_weight(w_bits, per_channel):
     """
     w_bits = np.asarray(w_bits, dtype=np.uint16)
     if not per_channel:
-        q, s = quant_dynamic(w_bits)
+        q, s = quant_dynamic(w_bits, fmt)
         return q, np.array([s], dtype=np.float32)
     w = bf16_bits_to_f32(w_bits)
     a = (np.max(np.abs(w), axis=1) if w.shape[1] else np.zeros(w.shape[0])).astype(np.float32)
-    # the per-tensor rule applied to each row: fl32(amax_n / 448), 1 when 0
-    s = np.where(a == 0, np.float32(1.0), a / _F32_MAX).astype(np.float32)
+    # the per-tensor rule applied to each row: fl32(amax_n / max), 1 when 0
+    s = np.where(a == 0, np.float32(1.0), a / FORMATS[fmt][2]).astype(np.float32)
     with np.errstate(over="ignore", divide="ignore", invalid="ignore"):
         v = (w / s[:, None]).astype(np.float32)
-    return encode(v), s
+    return FORMATS[fmt][1](v), s
 
 
-def gemm_exact(a_q, w_q):
-    """acc[m, n] = sum_k dec(A_q[m, k]) * dec(W_q[n, k]), exactly.
+def gemm_exact(a_q, w_q, fmt_a="e4m3", fmt_w="e4m3"):
+    """acc[m, n] = sum_k dec(A_q[m, k]) * dec(W_q[n, k]).
 
-    Every decoded value times 512 is an integer, so each product is an
-    integer multiple of 2^-18 below 448^2 and the float64 sum of K of them is
-    exact while K * 448^2 * 2^18 < 2^53, i.e. K < 171,196.
+    e4m3 x e4m3: every decoded value times 512 is an integer, so each
+    product is an integer multiple of 2^-18 below 448^2 and the float64 sum
+    of K of them is exact while K * 448^2 * 2^18 < 2^53, i.e. K < 171,196.
+    With an e5m2 operand (values are multiples of 2^-16 up to 57344) the
+    products span more than 53 bits, so the float64 sum may round: its error
+    is at most K * 2^-53 * sum_k |a_k w_k|, ten orders below the parity
+    tolerance.
     """
     a_q = np.asarray(a_q, dtype=np.uint8)
     w_q = np.asarray(w_q, dtype=np.uint8)
     k = a_q.shape[1]
-    if k >= 171196:
+    if fmt_a == "e4m3" and fmt_w == "e4m3" and k >= 171196:
         raise ValueError("K too large for the exact float64 path")
-    return decode(a_q) @ decode(w_q).T
+    return FORMATS[fmt_a][0](a_q) @ FORMATS[fmt_w][0](w_q).T
 
 
-def scaled_mm(a_q, w_q, s_a, s_w, per_channel, bias_bits=None, acc=None):
+def scaled_mm(a_q, w_q, s_a, s_w, per_channel, bias_bits=None, acc=None, fmt_a="e4m3", fmt_w="e4m3"):
     """The rescale epilogue in float64, unrounded.
 
     out[m, n] = acc[m, n] * s_a * s_w[n] (+ bias[n]); per tensor uses s_w[0]
@@ -120,7 +131,7 @@ def scaled_mm(a_q, w_q, s_a, s_w, per_channel, bias_bits=None, acc=None):
     per-tensor scaled GEMM followed by a rescale of column n.
     """
     if acc is None:
-        acc = gemm_exact(a_q, w_q)
+        acc = gemm_exact(a_q, w_q, fmt_a, fmt_w)
     s_w = np.asarray(s_w, dtype=np.float32).astype(np.float64)
     col = s_w if per_channel else np.full(acc.shape[1], s_w[0])
     out = acc * np.float64(np.float32(s_a)) * col[None, :]
@@ -129,9 +140,9 @@ def scaled_mm(a_q, w_q, s_a, s_w, per_channel, bias_bits=None, acc=None):
     return out
 
 
-def dequant_row_norms(q, scales, per_row):
+def dequant_row_norms(q, scales, per_row, fmt="e4m3"):
     """L2 norm of each dequantized row: ||dec(q[r, :]) * scale_r||_2 (fp64)."""
-    d = decode(np.asarray(q, dtype=np.uint8))
+    d = FORMATS[fmt][0](np.asarray(q, dtype=np.uint8))
     s = np.asarray(scales, dtype=np.float32).astype(np.float64)
     s = s if per_row else np.full(d.shape[0], s.reshape(-1)[0])
     return np.sqrt(np.sum(d * d, axis=1)) * np.abs(s)
