@@ -33,6 +33,10 @@ SIGNATURES = {
     "fp8_quant_static": (_I, [_P, _I64, _I64, _I64, _P, _P, _I64, _P]),
     "fp8_quant_dynamic_per_row": (_I, [_P, _I64, _I64, _I64, _P, _I64, _P, _P]),
     "fp8_scaled_mm": (_I, [_P, _I64, _P, _I64, _P, _P, _I, _I, _P, _P, _I64, _I64, _I64, _I64, _P]),
+    "fp8_quant_dynamic_fmt": (_I, [_P, _I64, _I64, _I64, _I, _P, _I64, _P, _P, _P]),
+    "fp8_quant_static_fmt": (_I, [_P, _I64, _I64, _I64, _I, _P, _P, _I64, _P]),
+    "fp8_quant_dynamic_per_row_fmt": (_I, [_P, _I64, _I64, _I64, _I, _P, _I64, _P, _P]),
+    "fp8_scaled_mm_fmt": (_I, [_P, _I64, _I, _P, _I64, _I, _P, _P, _I, _I, _P, _P, _I64, _I64, _I64, _I64, _P]),
     "fp8_norm_quant_workspace_bytes": (ctypes.c_size_t, [_I64]),
     "fp8_add_rmsnorm_quant_dynamic": (_I, [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, ctypes.c_float,
                                            _P, _I64, _P, _I64, _P, _P, _P]),
@@ -94,8 +98,11 @@ def new_workspace(device=None):
     return torch.empty(workspace_bytes(), dtype=torch.uint8, device=device or "cuda")
 
 
-def quant_dynamic(x, workspace=None, q=None, scale=None):
-    """Dynamic per-tensor quantization of bf16 x [rows, cols].
+FORMAT = {"e4m3": 0, "e5m2": 1}
+
+
+def quant_dynamic(x, workspace=None, q=None, scale=None, fmt="e4m3"):
+    """Dynamic per-tensor quantization of bf16 x [rows, cols] into fmt codes.
 
     Returns (q uint8 [rows, cols], scale float32 [1]); the scale stays on the
     device.
@@ -105,44 +112,45 @@ def quant_dynamic(x, workspace=None, q=None, scale=None):
     q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if q is None else q
     scale = torch.empty(1, dtype=torch.float32, device=x.device) if scale is None else scale
     workspace = new_workspace(x.device) if workspace is None else workspace
-    _check(lib().fp8_quant_dynamic(_ptr(x), rows, cols, x.stride(0), _ptr(q), q.stride(0), _ptr(scale),
-                                   _ptr(workspace), _stream()), "fp8_quant_dynamic")
+    _check(lib().fp8_quant_dynamic_fmt(_ptr(x), rows, cols, x.stride(0), FORMAT[fmt], _ptr(q), q.stride(0),
+                                       _ptr(scale), _ptr(workspace), _stream()), "fp8_quant_dynamic")
     return q, scale
 
 
-def quant_static(x, scale, q=None):
+def quant_static(x, scale, q=None, fmt="e4m3"):
     """Quantize bf16 x with a given device float32 scale; returns q uint8."""
     _mat(x, "x", torch.bfloat16)
     rows, cols = x.shape
     q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if q is None else q
-    _check(lib().fp8_quant_static(_ptr(x), rows, cols, x.stride(0), _ptr(scale), _ptr(q), q.stride(0),
-                                  _stream()), "fp8_quant_static")
+    _check(lib().fp8_quant_static_fmt(_ptr(x), rows, cols, x.stride(0), FORMAT[fmt], _ptr(scale), _ptr(q),
+                                      q.stride(0), _stream()), "fp8_quant_static")
     return q
 
 
-def quant_dynamic_per_row(x, q=None, scales=None):
+def quant_dynamic_per_row(x, q=None, scales=None, fmt="e4m3"):
     """One scale per row (channelwise weight quantization): (q, scales [rows])."""
     _mat(x, "x", torch.bfloat16)
     rows, cols = x.shape
     q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if q is None else q
     scales = torch.empty(rows, dtype=torch.float32, device=x.device) if scales is None else scales
-    _check(lib().fp8_quant_dynamic_per_row(_ptr(x), rows, cols, x.stride(0), _ptr(q), q.stride(0),
-                                           _ptr(scales), _stream()), "fp8_quant_dynamic_per_row")
+    _check(lib().fp8_quant_dynamic_per_row_fmt(_ptr(x), rows, cols, x.stride(0), FORMAT[fmt], _ptr(q), q.stride(0),
+                                               _ptr(scales), _stream()), "fp8_quant_dynamic_per_row")
     return q, scales
 
 
-def quant_weight(w, per_channel):
+def quant_weight(w, per_channel, fmt="e4m3"):
     """Load-time weight quantization on the device: (w_q, s_w)."""
     if per_channel:
-        return quant_dynamic_per_row(w)
-    return quant_dynamic(w)
+        return quant_dynamic_per_row(w, fmt=fmt)
+    return quant_dynamic(w, fmt=fmt)
 
 
-def scaled_mm(a_q, w_q, s_a, s_w, per_channel, bias=None, out=None, accum="fp32"):
+def scaled_mm(a_q, w_q, s_a, s_w, per_channel, bias=None, out=None, accum="fp32", fmt_a="e4m3", fmt_w="e4m3"):
     """out[M, N] = bf16((A_q @ W_q^T) * s_a * s_w (+ bias)); W_q is [N, K].
 
     accum: "fp32" (fp32-class sums, default) or "fp8" (fp8 matrix cores for
-    M > 16: twice the rate, 13-bit sums inside each group of 8 products).
+    M > 64: twice the rate, 13-bit sums inside each group of 8 products).
+    fmt_a / fmt_w: "e4m3" or "e5m2" codes.
     """
     _mat(a_q, "a_q", torch.uint8)
     _mat(w_q, "w_q", torch.uint8)
@@ -152,16 +160,17 @@ def scaled_mm(a_q, w_q, s_a, s_w, per_channel, bias=None, out=None, accum="fp32"
         raise ValueError(f"K mismatch: a_q has {K}, w_q has {K2}")
     out = torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device) if out is None else out
     mode = FP8_SCALE_PER_CHANNEL if per_channel else FP8_SCALE_PER_TENSOR
-    _check(lib().fp8_scaled_mm(_ptr(a_q), a_q.stride(0), _ptr(w_q), w_q.stride(0), _ptr(s_a), _ptr(s_w), mode,
-                               ACCUM[accum], _ptr(bias), _ptr(out), out.stride(0), M, N, K, _stream()),
+    _check(lib().fp8_scaled_mm_fmt(_ptr(a_q), a_q.stride(0), FORMAT[fmt_a], _ptr(w_q), w_q.stride(0),
+                                   FORMAT[fmt_w], _ptr(s_a), _ptr(s_w), mode, ACCUM[accum], _ptr(bias), _ptr(out),
+                                   out.stride(0), M, N, K, _stream()),
            "fp8_scaled_mm")
     return out
 
 
-def linear(x, w_q, s_w, per_channel, bias=None, workspace=None, accum="fp32"):
+def linear(x, w_q, s_w, per_channel, bias=None, workspace=None, accum="fp32", fmt_a="e4m3", fmt_w="e4m3"):
     """The W8A8 linear: dynamic activation quantization then scaled GEMM."""
-    a_q, s_a = quant_dynamic(x, workspace=workspace)
-    return scaled_mm(a_q, w_q, s_a, s_w, per_channel, bias, accum=accum)
+    a_q, s_a = quant_dynamic(x, workspace=workspace, fmt=fmt_a)
+    return scaled_mm(a_q, w_q, s_a, s_w, per_channel, bias, accum=accum, fmt_a=fmt_a, fmt_w=fmt_w)
 
 
 def norm_workspace(rows, device=None):

@@ -42,6 +42,11 @@ fp8_status check_quant(const char* fn, const uint16_t* x, int64_t rows, int64_t 
   return FP8_OK;
 }
 
+fp8_status check_fmt(const char* fn, fp8_format f) {
+  if (f != FP8_FORMAT_E4M3 && f != FP8_FORMAT_E5M2) return fail(FP8_ERR_INVALID_ARG, "%s: unknown format %d", fn, (int)f);
+  return FP8_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -50,38 +55,56 @@ size_t fp8_quant_workspace_bytes(void) { return fp8w8a8::quant_workspace_bytes()
 
 const char* fp8_last_error(void) { return g_err; }
 
-fp8_status fp8_quant_dynamic(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q_e4m3,
-                             int64_t ld_q, float* scale_out, void* workspace, void* stream) {
+fp8_status fp8_quant_dynamic_fmt(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, fp8_format fmt,
+                                 uint8_t* q, int64_t ld_q, float* scale_out, void* workspace, void* stream) {
   const char* fn = "fp8_quant_dynamic";
-  fp8_status st = check_quant(fn, x_bf16, rows, cols, ld_x, q_e4m3, ld_q);
+  fp8_status st = check_quant(fn, x_bf16, rows, cols, ld_x, q, ld_q);
+  if (st == FP8_OK) st = check_fmt(fn, fmt);
   if (st != FP8_OK) return st;
   if (scale_out == nullptr) return fail(FP8_ERR_INVALID_ARG, "%s: null scale_out", fn);
   if (rows > 0 && cols > 0 && workspace == nullptr) return fail(FP8_ERR_INVALID_ARG, "%s: null workspace", fn);
-  return hip_status(fp8w8a8::launch_quant_dynamic(x_bf16, rows, cols, ld_x, q_e4m3, ld_q, scale_out, workspace,
+  return hip_status(fp8w8a8::launch_quant_dynamic(x_bf16, rows, cols, ld_x, (int)fmt, q, ld_q, scale_out, workspace,
                                                   static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+fp8_status fp8_quant_dynamic(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q_e4m3,
+                             int64_t ld_q, float* scale_out, void* workspace, void* stream) {
+  return fp8_quant_dynamic_fmt(x_bf16, rows, cols, ld_x, FP8_FORMAT_E4M3, q_e4m3, ld_q, scale_out, workspace, stream);
+}
+
+fp8_status fp8_quant_static_fmt(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, fp8_format fmt,
+                                const float* scale, uint8_t* q, int64_t ld_q, void* stream) {
+  const char* fn = "fp8_quant_static";
+  fp8_status st = check_quant(fn, x_bf16, rows, cols, ld_x, q, ld_q);
+  if (st == FP8_OK) st = check_fmt(fn, fmt);
+  if (st != FP8_OK) return st;
+  if (scale == nullptr) return fail(FP8_ERR_INVALID_ARG, "%s: null scale", fn);
+  return hip_status(fp8w8a8::launch_quant_static(x_bf16, rows, cols, ld_x, (int)fmt, scale, q, ld_q,
+                                                 static_cast<hipStream_t>(stream)),
                     fn);
 }
 
 fp8_status fp8_quant_static(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, const float* scale,
                             uint8_t* q_e4m3, int64_t ld_q, void* stream) {
-  const char* fn = "fp8_quant_static";
-  fp8_status st = check_quant(fn, x_bf16, rows, cols, ld_x, q_e4m3, ld_q);
+  return fp8_quant_static_fmt(x_bf16, rows, cols, ld_x, FP8_FORMAT_E4M3, scale, q_e4m3, ld_q, stream);
+}
+
+fp8_status fp8_quant_dynamic_per_row_fmt(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                                         fp8_format fmt, uint8_t* q, int64_t ld_q, float* scales_out, void* stream) {
+  const char* fn = "fp8_quant_dynamic_per_row";
+  fp8_status st = check_quant(fn, x_bf16, rows, cols, ld_x, q, ld_q);
+  if (st == FP8_OK) st = check_fmt(fn, fmt);
   if (st != FP8_OK) return st;
-  if (scale == nullptr) return fail(FP8_ERR_INVALID_ARG, "%s: null scale", fn);
-  return hip_status(fp8w8a8::launch_quant_static(x_bf16, rows, cols, ld_x, scale, q_e4m3, ld_q,
-                                                 static_cast<hipStream_t>(stream)),
+  if (rows > 0 && scales_out == nullptr) return fail(FP8_ERR_INVALID_ARG, "%s: null scales_out", fn);
+  return hip_status(fp8w8a8::launch_quant_per_row(x_bf16, rows, cols, ld_x, (int)fmt, q, ld_q, scales_out,
+                                                  static_cast<hipStream_t>(stream)),
                     fn);
 }
 
 fp8_status fp8_quant_dynamic_per_row(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
                                      uint8_t* q_e4m3, int64_t ld_q, float* scales_out, void* stream) {
-  const char* fn = "fp8_quant_dynamic_per_row";
-  fp8_status st = check_quant(fn, x_bf16, rows, cols, ld_x, q_e4m3, ld_q);
-  if (st != FP8_OK) return st;
-  if (rows > 0 && scales_out == nullptr) return fail(FP8_ERR_INVALID_ARG, "%s: null scales_out", fn);
-  return hip_status(fp8w8a8::launch_quant_per_row(x_bf16, rows, cols, ld_x, q_e4m3, ld_q, scales_out,
-                                                  static_cast<hipStream_t>(stream)),
-                    fn);
+  return fp8_quant_dynamic_per_row_fmt(x_bf16, rows, cols, ld_x, FP8_FORMAT_E4M3, q_e4m3, ld_q, scales_out, stream);
 }
 
 size_t fp8_norm_quant_workspace_bytes(int64_t rows) {
@@ -129,10 +152,12 @@ fp8_status fp8_silu_mul_quant_dynamic(const uint16_t* gu_bf16, int64_t ld_gu, in
                     fn);
 }
 
-fp8_status fp8_scaled_mm(const uint8_t* a_q, int64_t lda, const uint8_t* w_q, int64_t ldw, const float* s_a,
-                         const float* s_w, fp8_scale_mode mode, fp8_accum_mode accum, const uint16_t* bias_bf16,
-                         uint16_t* out_bf16, int64_t ldo, int64_t M, int64_t N, int64_t K, void* stream) {
+fp8_status fp8_scaled_mm_fmt(const uint8_t* a_q, int64_t lda, fp8_format fmt_a, const uint8_t* w_q, int64_t ldw,
+                             fp8_format fmt_w, const float* s_a, const float* s_w, fp8_scale_mode mode,
+                             fp8_accum_mode accum, const uint16_t* bias_bf16, uint16_t* out_bf16, int64_t ldo,
+                             int64_t M, int64_t N, int64_t K, void* stream) {
   const char* fn = "fp8_scaled_mm";
+  if (check_fmt(fn, fmt_a) != FP8_OK || check_fmt(fn, fmt_w) != FP8_OK) return FP8_ERR_INVALID_ARG;
   if (M < 0 || N < 0) return fail(FP8_ERR_INVALID_ARG, "%s: negative M or N (M=%lld, N=%lld)", fn,
                                   (long long)M, (long long)N);
   if (K < 1) return fail(FP8_ERR_INVALID_ARG, "%s: K must be >= 1 (K=%lld)", fn, (long long)K);
@@ -153,6 +178,8 @@ fp8_status fp8_scaled_mm(const uint8_t* a_q, int64_t lda, const uint8_t* w_q, in
   g.lda = lda; g.ldw = ldw; g.ldo = ldo;
   g.M = (int32_t)M; g.N = (int32_t)N; g.K = (int32_t)K;
   g.per_channel = mode == FP8_SCALE_PER_CHANNEL ? 1 : 0;
+  g.fmt_a = (int32_t)fmt_a;
+  g.fmt_w = (int32_t)fmt_w;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
@@ -170,6 +197,13 @@ fp8_status fp8_scaled_mm(const uint8_t* a_q, int64_t lda, const uint8_t* w_q, in
     if (st != FP8_OK) return st;
   }
   return FP8_OK;
+}
+
+fp8_status fp8_scaled_mm(const uint8_t* a_q, int64_t lda, const uint8_t* w_q, int64_t ldw, const float* s_a,
+                         const float* s_w, fp8_scale_mode mode, fp8_accum_mode accum, const uint16_t* bias_bf16,
+                         uint16_t* out_bf16, int64_t ldo, int64_t M, int64_t N, int64_t K, void* stream) {
+  return fp8_scaled_mm_fmt(a_q, lda, FP8_FORMAT_E4M3, w_q, ldw, FP8_FORMAT_E4M3, s_a, s_w, mode, accum, bias_bf16,
+                           out_bf16, ldo, M, N, K, stream);
 }
 
 }  // extern "C"

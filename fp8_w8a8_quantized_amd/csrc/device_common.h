@@ -14,6 +14,16 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kE4M3Max = 448.0f;
+constexpr float kE5M2Max = 57344.0f;
+
+// fp8 formats: e4m3 (OCP E4M3, finite-only variant, the pages' format) and
+// e5m2 (OCP E5M2, the extension named on the compressed-tensors fp8 page).
+enum Fmt : int { kE4M3 = 0, kE5M2 = 1 };
+
+template <int F>
+__device__ __forceinline__ constexpr float fmt_max() {
+  return F == kE5M2 ? kE5M2Max : kE4M3Max;
+}
 
 // s_waitcnt immediate for gfx9: lgkmcnt(0), vmcnt and expcnt left at max.
 constexpr int kWaitLgkm0 = 0xC07F;
@@ -33,39 +43,59 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u & 0x7fffffffu) > 0x7f800000u ? quiet_nan : rounded;
 }
 
-// Per-tensor scale from amax: amax / 448 correctly rounded in float32; an
-// all-zero tensor has no range to map and takes scale 1.
+// Per-tensor scale from amax: amax / max(format) correctly rounded in
+// float32; an all-zero tensor has no range to map and takes scale 1.
+template <int F = kE4M3>
 __device__ __forceinline__ float scale_from_amax(float amax) {
-  return amax == 0.0f ? 1.0f : amax / kE4M3Max;
+  return amax == 0.0f ? 1.0f : amax / fmt_max<F>();
 }
 
-// Saturating round-to-nearest-even e4m3fn codes for four values divided by s.
-// The division is the correctly rounded float32 one (the compiler's default
-// for '/'), then the quotient is clamped to +-448 and converted by the
-// hardware's fp8 conversion, which rounds to nearest even (OCP E4M3 codes on
-// gfx950) but turns magnitudes past 464 into NaN -- hence the clamp.
+// Two fp8 codes packed into byte pair `hi` of `old`: the hardware's fp8
+// (e4m3) or bf8 (e5m2) conversion, both round to nearest even on gfx950.
+template <int F, bool HI>
+__device__ __forceinline__ uint32_t cvt_pk(float a, float b, uint32_t old) {
+  if constexpr (F == kE5M2)
+    return __builtin_amdgcn_cvt_pk_bf8_f32(a, b, old, HI);
+  else
+    return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+}
+
+// Saturating round-to-nearest-even codes for four values divided by s.  The
+// division is the correctly rounded float32 one (the compiler's default for
+// '/'), then the quotient is clamped to +-max and converted by the hardware,
+// which rounds to nearest even (OCP codes on gfx950) but does not saturate
+// (e4m3: past 464 gives NaN; e5m2: past 61440 gives infinity) -- hence the
+// clamp.
+template <int F = kE4M3>
 __device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, float s) {
-  float qa = __builtin_amdgcn_fmed3f(a / s, -kE4M3Max, kE4M3Max);
-  float qb = __builtin_amdgcn_fmed3f(b / s, -kE4M3Max, kE4M3Max);
-  float qc = __builtin_amdgcn_fmed3f(c / s, -kE4M3Max, kE4M3Max);
-  float qd = __builtin_amdgcn_fmed3f(d / s, -kE4M3Max, kE4M3Max);
-  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(qa, qb, 0, false);
-  return __builtin_amdgcn_cvt_pk_fp8_f32(qc, qd, w, true);
+  constexpr float M = fmt_max<F>();
+  float qa = __builtin_amdgcn_fmed3f(a / s, -M, M);
+  float qb = __builtin_amdgcn_fmed3f(b / s, -M, M);
+  float qc = __builtin_amdgcn_fmed3f(c / s, -M, M);
+  float qd = __builtin_amdgcn_fmed3f(d / s, -M, M);
+  uint32_t w = cvt_pk<F, false>(qa, qb, 0);
+  return cvt_pk<F, true>(qc, qd, w);
 }
 
-__device__ __forceinline__ uint32_t quant1(float a, float s) {
-  float q = __builtin_amdgcn_fmed3f(a / s, -kE4M3Max, kE4M3Max);
-  return __builtin_amdgcn_cvt_pk_fp8_f32(q, 0.0f, 0, false) & 0xffu;
-}
-
-// Quantize 8 bf16 values packed in a 16-byte word into 8 e4m3fn bytes.
+// Quantize 8 bf16 values packed in a 16-byte word into 8 fp8 bytes.
+template <int F = kE4M3>
 __device__ __forceinline__ uint2 quant8(v4i x, float s) {
   uint2 r;
-  r.x = quant4(bf16_to_f32(x[0] & 0xffff), bf16_to_f32((uint32_t)x[0] >> 16),
-               bf16_to_f32(x[1] & 0xffff), bf16_to_f32((uint32_t)x[1] >> 16), s);
-  r.y = quant4(bf16_to_f32(x[2] & 0xffff), bf16_to_f32((uint32_t)x[2] >> 16),
-               bf16_to_f32(x[3] & 0xffff), bf16_to_f32((uint32_t)x[3] >> 16), s);
+  r.x = quant4<F>(bf16_to_f32(x[0] & 0xffff), bf16_to_f32((uint32_t)x[0] >> 16),
+                  bf16_to_f32(x[1] & 0xffff), bf16_to_f32((uint32_t)x[1] >> 16), s);
+  r.y = quant4<F>(bf16_to_f32(x[2] & 0xffff), bf16_to_f32((uint32_t)x[2] >> 16),
+                  bf16_to_f32(x[3] & 0xffff), bf16_to_f32((uint32_t)x[3] >> 16), s);
   return r;
+}
+
+// 4 fp8 codes (one 32-bit word) -> 2 x 2 bf16 values, exactly (every e4m3
+// and every finite e5m2 value is a bf16 value; the scale is 1).
+template <int F, bool HI>
+__device__ __forceinline__ bf16x2 fp8x2_to_bf16(int w) {
+  if constexpr (F == kE5M2)
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, HI);
+  else
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
 }
 
 // Largest |bf16| among 8 packed values, as the 15-bit magnitude pattern.

@@ -88,17 +88,20 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* base, int row, int chunk
   return f;
 }
 
-// 4 e4m3 codes -> 4 bf16 values of dst starting at element `at` (exact).
-__device__ __forceinline__ void e4m3x4_to_bf16(int w, bf16x8& dst, int at) {
-  bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
-  bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+// 4 fp8 codes of format F -> 4 bf16 values of dst starting at element `at`
+// (exact).
+template <int F>
+__device__ __forceinline__ void fp8x4_to_bf16(int w, bf16x8& dst, int at) {
+  bf16x2 lo = fp8x2_to_bf16<F, false>(w);
+  bf16x2 hi = fp8x2_to_bf16<F, true>(w);
   dst[at] = lo[0]; dst[at + 1] = lo[1]; dst[at + 2] = hi[0]; dst[at + 3] = hi[1];
 }
 
+template <int F>
 __device__ __forceinline__ bf16x8 slice_bf16(const v8i& f, int t) {
   bf16x8 b;
-  e4m3x4_to_bf16(f[2 * t], b, 0);
-  e4m3x4_to_bf16(f[2 * t + 1], b, 4);
+  fp8x4_to_bf16<F>(f[2 * t], b, 0);
+  fp8x4_to_bf16<F>(f[2 * t + 1], b, 4);
   return b;
 }
 
@@ -136,7 +139,7 @@ __device__ __forceinline__ Tile tile_at(const GemmArgs& g, int b, int tiles_m, i
 
 // VEC: N % 8 == 0, ldo % 8 == 0 and a 16-byte aligned output, so every lane
 // writes whole 16-byte chunks (a fixed count of stores per tile).
-template <bool EXACT, bool VEC>
+template <bool EXACT, bool VEC, int FA, int FW>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStageBytes + kEpiParamBytes];
   // the tile's 256 column scales (fp32) and biases (bf16), loaded by DMA
@@ -268,8 +271,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
           for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[ks][i], af[ks][j], acc[i][j], 0, 0, 0,
-                                                                           0, 0, 0);
+              // operand formats: cbsz for the A operand (W), blgp for B (A_q); 0 = fp8, 1 = bf8
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[ks][i], af[ks][j], acc[i][j], FW, FA,
+                                                                           0, 0, 0, 0);
         } else {
           // the lane's 32 k-values in four slices of 8 (same slicing for
           // both operands), one bf16 32x32x16 product per slice
@@ -277,9 +281,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
           for (int t = 0; t < 4; ++t) {
             bf16x8 wb[4], ab[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) wb[i] = slice_bf16(wf[ks][i], t);
+            for (int i = 0; i < 4; ++i) wb[i] = slice_bf16<FW>(wf[ks][i], t);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ab[j] = slice_bf16(af[ks][j], t);
+            for (int j = 0; j < 4; ++j) ab[j] = slice_bf16<FA>(af[ks][j], t);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -381,23 +385,32 @@ bool gemm_mfma_supported(const GemmArgs& g) {
          (int64_t)BM * g.ldo * 2 < (1ll << 31) && ((uintptr_t)g.out % 2 == 0) && g.N < (1 << 29);
 }
 
-hipError_t launch_gemm_mfma(const GemmArgs& g, bool fp8_accumulate, hipStream_t stream) {
+template <int FA, int FW>
+hipError_t launch_mfma(const GemmArgs& g, bool fp8_accumulate, hipStream_t stream) {
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   const int T = tiles_m * tiles_n;
   const unsigned grid = (unsigned)min(T, cu_count());
   const bool vec = (g.N % 8 == 0) && (g.ldo % 8 == 0) && ((uintptr_t)g.out % 16 == 0);
   if (fp8_accumulate) {
     if (vec)
-      gemm_mfma_kernel<false, true><<<grid, kThreads, 0, stream>>>(g, tiles_m, tiles_n);
+      gemm_mfma_kernel<false, true, FA, FW><<<grid, kThreads, 0, stream>>>(g, tiles_m, tiles_n);
     else
-      gemm_mfma_kernel<false, false><<<grid, kThreads, 0, stream>>>(g, tiles_m, tiles_n);
+      gemm_mfma_kernel<false, false, FA, FW><<<grid, kThreads, 0, stream>>>(g, tiles_m, tiles_n);
   } else {
     if (vec)
-      gemm_mfma_kernel<true, true><<<grid, kThreads, 0, stream>>>(g, tiles_m, tiles_n);
+      gemm_mfma_kernel<true, true, FA, FW><<<grid, kThreads, 0, stream>>>(g, tiles_m, tiles_n);
     else
-      gemm_mfma_kernel<true, false><<<grid, kThreads, 0, stream>>>(g, tiles_m, tiles_n);
+      gemm_mfma_kernel<true, false, FA, FW><<<grid, kThreads, 0, stream>>>(g, tiles_m, tiles_n);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_mfma(const GemmArgs& g, bool fp8_accumulate, hipStream_t stream) {
+  if (g.fmt_a == kE5M2)
+    return g.fmt_w == kE5M2 ? launch_mfma<kE5M2, kE5M2>(g, fp8_accumulate, stream)
+                            : launch_mfma<kE5M2, kE4M3>(g, fp8_accumulate, stream);
+  return g.fmt_w == kE5M2 ? launch_mfma<kE4M3, kE5M2>(g, fp8_accumulate, stream)
+                          : launch_mfma<kE4M3, kE4M3>(g, fp8_accumulate, stream);
 }
 
 }  // namespace fp8w8a8

@@ -82,23 +82,26 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* row, int k0s, int g, int
   return f;
 }
 
-// 4 e4m3 codes (one 32-bit word) -> 4 bf16 values, exactly (scale 1).
-__device__ __forceinline__ void e4m3x4_to_bf16(int w, bf16x8& dst, int at) {
-  bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
-  bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+// 4 fp8 codes (one 32-bit word) of format F -> 4 bf16 values, exactly.
+template <int F>
+__device__ __forceinline__ void fp8x4_to_bf16(int w, bf16x8& dst, int at) {
+  bf16x2 lo = fp8x2_to_bf16<F, false>(w);
+  bf16x2 hi = fp8x2_to_bf16<F, true>(w);
   dst[at] = lo[0]; dst[at + 1] = lo[1]; dst[at + 2] = hi[0]; dst[at + 3] = hi[1];
 }
 
-// acc += W_frag . A_frag over 32 e4m3 k-values per lane, as four bf16
-// 16x16x32 products (k-values 8t..8t+7 of the lane feed instruction t).
-__device__ __forceinline__ v4f mfma_e4m3_as_bf16(v8i wf, v8i af, v4f acc) {
+// acc += W_frag . A_frag over 32 fp8 k-values per lane (W in format FW, A
+// in FA), as four bf16 16x16x32 products (k-values 8t..8t+7 of the lane feed
+// instruction t).
+template <int FA, int FW>
+__device__ __forceinline__ v4f mfma_fp8_as_bf16(v8i wf, v8i af, v4f acc) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     bf16x8 wb, ab;
-    e4m3x4_to_bf16(wf[2 * t], wb, 0);
-    e4m3x4_to_bf16(wf[2 * t + 1], wb, 4);
-    e4m3x4_to_bf16(af[2 * t], ab, 0);
-    e4m3x4_to_bf16(af[2 * t + 1], ab, 4);
+    fp8x4_to_bf16<FW>(wf[2 * t], wb, 0);
+    fp8x4_to_bf16<FW>(wf[2 * t + 1], wb, 4);
+    fp8x4_to_bf16<FA>(af[2 * t], ab, 0);
+    fp8x4_to_bf16<FA>(af[2 * t + 1], ab, 4);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, ab, acc, 0, 0, 0);
   }
   return acc;
@@ -176,7 +179,7 @@ constexpr int kStageBytesPerWave = 2 * 16 * 256;
 
 inline size_t skinny_lds_bytes(int nw) { return (size_t)nw * (kStageBytesPerWave + 4 * 64 * sizeof(float)); }
 
-template <int P>
+template <int P, int FA, int FW>
 __global__ __launch_bounds__(kMaxWaves * 64) void gemm_skinny_kernel(GemmArgs g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
   const int NW = blockDim.x >> 6;
@@ -240,7 +243,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemm_skinny_kernel(GemmArgs g)
         const v4i whi = *reinterpret_cast<const v4i*>(LW + r * 256 + ((c1 ^ r) << 4));
         const v4i alo = *reinterpret_cast<const v4i*>(LA + r * 256 + ((c0 ^ r) << 4));
         const v4i ahi = *reinterpret_cast<const v4i*>(LA + r * 256 + ((c1 ^ r) << 4));
-        acc = mfma_e4m3_as_bf16(cat8(wlo, whi), cat8(alo, ahi), acc);
+        acc = mfma_fp8_as_bf16<FA, FW>(cat8(wlo, whi), cat8(alo, ahi), acc);
       }
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       __builtin_amdgcn_wave_barrier();
@@ -249,7 +252,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemm_skinny_kernel(GemmArgs g)
   reduce_and_store(g, acc, red, NW, wave, lane, n0, m0, ep);
 }
 
-template <int NW, int U, bool VEC>
+template <int NW, int U, bool VEC, int FA, int FW>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_generic_kernel(GemmArgs g) {
   __shared__ float red[NW][4][64];
   const int lane = threadIdx.x & 63;
@@ -272,22 +275,21 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_generic_kernel(GemmArgs g
       af[u] = load_frag<VEC>(arow, s * 128, grp, g.K, m_ok && s < ks);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) acc = mfma_e4m3_as_bf16(wf[u], af[u], acc);
+    for (int u = 0; u < U; ++u) acc = mfma_fp8_as_bf16<FA, FW>(wf[u], af[u], acc);
   }
 
   reduce_and_store(g, acc, red, NW, wave, lane, n0, m0, ep);
 }
 
-template <int NW>
+template <int NW, int FA, int FW>
 hipError_t launch_generic(const GemmArgs& g, dim3 grid, hipStream_t stream) {
   constexpr int U = NW >= 16 ? 4 : 8;  // 16 waves leave 128 VGPRs per lane
-  gemm_skinny_generic_kernel<NW, U, false><<<grid, NW * 64, 0, stream>>>(g);
+  gemm_skinny_generic_kernel<NW, U, false, FA, FW><<<grid, NW * 64, 0, stream>>>(g);
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_gemm_skinny(const GemmArgs& g, hipStream_t stream) {
+template <int FA, int FW>
+hipError_t launch_skinny(const GemmArgs& g, hipStream_t stream) {
   const bool aligned = ((uintptr_t)g.a % 16 == 0) && ((uintptr_t)g.w % 16 == 0) && (g.lda % 16 == 0) &&
                        (g.ldw % 16 == 0) && (g.K % 16 == 0);
   const int64_t tiles_n = (g.N + 15) / 16, tiles_m = (g.M + 15) / 16;
@@ -296,11 +298,11 @@ hipError_t launch_gemm_skinny(const GemmArgs& g, hipStream_t stream) {
     // 8 waves for long K (more bytes in flight per workgroup), else 4
     // dynamic LDS above 64 KiB must be allowed once per process
     static const hipError_t lds_attr = hipFuncSetAttribute(
-        (const void*)gemm_skinny_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize,
+        (const void*)gemm_skinny_kernel<2, FA, FW>, hipFuncAttributeMaxDynamicSharedMemorySize,
         (int)skinny_lds_bytes(kMaxWaves));
     if (lds_attr != hipSuccess) return lds_attr;
     const int nw = (g.K + 255) / 256 >= 32 ? 8 : 4;
-    gemm_skinny_kernel<2><<<grid, nw * 64, skinny_lds_bytes(nw), stream>>>(g);
+    gemm_skinny_kernel<2, FA, FW><<<grid, nw * 64, skinny_lds_bytes(nw), stream>>>(g);
     return hipGetLastError();
   }
   const int64_t tiles = tiles_n * tiles_m;
@@ -308,12 +310,20 @@ hipError_t launch_gemm_skinny(const GemmArgs& g, hipStream_t stream) {
   int nw = tiles >= 256 ? 4 : (tiles >= 128 ? 8 : 16);
   while (nw > 1 && nw > ks) nw >>= 1;
   switch (nw) {
-    case 16: return launch_generic<16>(g, grid, stream);
-    case 8: return launch_generic<8>(g, grid, stream);
-    case 4: return launch_generic<4>(g, grid, stream);
-    case 2: return launch_generic<2>(g, grid, stream);
-    default: return launch_generic<1>(g, grid, stream);
+    case 16: return launch_generic<16, FA, FW>(g, grid, stream);
+    case 8: return launch_generic<8, FA, FW>(g, grid, stream);
+    case 4: return launch_generic<4, FA, FW>(g, grid, stream);
+    case 2: return launch_generic<2, FA, FW>(g, grid, stream);
+    default: return launch_generic<1, FA, FW>(g, grid, stream);
   }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_skinny(const GemmArgs& g, hipStream_t stream) {
+  if (g.fmt_a == kE5M2)
+    return g.fmt_w == kE5M2 ? launch_skinny<kE5M2, kE5M2>(g, stream) : launch_skinny<kE5M2, kE4M3>(g, stream);
+  return g.fmt_w == kE5M2 ? launch_skinny<kE4M3, kE5M2>(g, stream) : launch_skinny<kE4M3, kE4M3>(g, stream);
 }
 
 }  // namespace fp8w8a8

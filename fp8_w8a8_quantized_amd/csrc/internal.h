@@ -10,10 +10,11 @@ namespace fp8w8a8 {
 
 size_t quant_workspace_bytes();
 
-hipError_t launch_quant_dynamic(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
+// fmt: 0 = e4m3, 1 = e5m2 (codes written and the scale's denominator).
+hipError_t launch_quant_dynamic(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int fmt, uint8_t* q,
                                 int64_t ld_q, float* scale_out, void* workspace, hipStream_t stream);
-hipError_t launch_quant_static(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, const float* scale,
-                               uint8_t* q, int64_t ld_q, hipStream_t stream);
+hipError_t launch_quant_static(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
+                               const float* scale, uint8_t* q, int64_t ld_q, hipStream_t stream);
 // Fused producers (chained-linears glue) + dynamic per-tensor quantization.
 size_t norm_quant_workspace_bytes(int64_t rows);
 hipError_t launch_add_rmsnorm_quant(const uint16_t* h, int64_t ld_h, const uint16_t* delta, int64_t ld_delta,
@@ -23,7 +24,7 @@ hipError_t launch_add_rmsnorm_quant(const uint16_t* h, int64_t ld_h, const uint1
 hipError_t launch_silu_mul_quant(const uint16_t* gu, int64_t ld_gu, int64_t rows, int64_t cols, uint16_t* y_out,
                                  int64_t ld_y, uint8_t* q, int64_t ld_q, float* scale_out, void* workspace,
                                  hipStream_t stream);
-hipError_t launch_quant_per_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
+hipError_t launch_quant_per_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int fmt, uint8_t* q,
                                 int64_t ld_q, float* scales_out, hipStream_t stream);
 
 struct GemmArgs {
@@ -36,6 +37,7 @@ struct GemmArgs {
   int64_t lda, ldw, ldo;
   int32_t M, N, K;
   int32_t per_channel;
+  int32_t fmt_a, fmt_w;  // 0 = e4m3, 1 = e5m2
 };
 
 // Skinny path: any layout; one 16-row block of M per grid row.

@@ -52,9 +52,10 @@ __device__ __forceinline__ void unit_coords(const QuantArgs& a, uint32_t u, uint
   c0 = (u - r * a.units_per_row) * 8;
 }
 
+template <int F>
 __device__ __forceinline__ void unit_store(const QuantArgs& a, uint32_t r, uint32_t c0, v4i x, float s) {
   uint8_t* qrow = a.q + (int64_t)r * a.ld_q;
-  const uint2 v = quant8(x, s);
+  const uint2 v = quant8<F>(x, s);
   if (a.vec_q && c0 + 8 <= a.cols) {
     *reinterpret_cast<uint2*>(qrow + c0) = v;
     return;
@@ -205,7 +206,7 @@ __device__ __forceinline__ uint32_t absmax_range(const QuantArgs& a, const Src& 
   return m;
 }
 
-template <class Src>
+template <int F, class Src>
 __device__ __forceinline__ void quant_range(const QuantArgs& a, const Src& src, uint32_t u0, uint32_t u1,
                                             uint32_t stride, float s) {
   for (uint32_t u = u0; u < u1; u += stride * kUnroll) {
@@ -224,7 +225,7 @@ __device__ __forceinline__ void quant_range(const QuantArgs& a, const Src& src, 
     for (int i = 0; i < kUnroll; ++i)
       if (u + i * stride < u1) {
         src.emit(a, r[i], c0[i], v[i]);
-        unit_store(a, r[i], c0[i], v[i], s);
+        unit_store<F>(a, r[i], c0[i], v[i], s);
       }
   }
 }
@@ -237,7 +238,7 @@ __device__ __forceinline__ void quant_range(const QuantArgs& a, const Src& src, 
 // workgroup evaluates the source over the whole tensor.
 constexpr int kSmallThreads = 1024;
 constexpr int kSmallBatch = 8;
-template <class Src>
+template <int F, class Src>
 __global__ __launch_bounds__(kSmallThreads) void quant_dynamic_small_kernel(QuantArgs a, Src src, float* scale_out) {
   __shared__ uint32_t red[16];
   const uint32_t T = a.total_units;
@@ -263,14 +264,14 @@ __global__ __launch_bounds__(kSmallThreads) void quant_dynamic_small_kernel(Quan
     }
   }
   m = block_max_u32(m, red);
-  const float s = scale_from_amax(bf16_to_f32(m));
+  const float s = scale_from_amax<F>(bf16_to_f32(m));
   if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
   const uint32_t u = threadIdx.x + blockIdx.x * kSmallThreads;
   if (u < T) {
     uint32_t r, c0;
     unit_coords(a, u, r, c0);
     src.emit(a, r, c0, keep);
-    unit_store(a, r, c0, keep, s);
+    unit_store<F>(a, r, c0, keep, s);
   }
 }
 
@@ -284,33 +285,35 @@ __global__ __launch_bounds__(256) void absmax_partial_kernel(QuantArgs a, Src sr
 }
 
 // Launch 2 of 2: fold the maxima, derive the scale, quantize.
-template <class Src>
+template <int F, class Src>
 __global__ __launch_bounds__(256) void quant_from_partial_kernel(QuantArgs a, Src src, const uint32_t* partial,
                                                                   uint32_t nparts, float* scale_out) {
   __shared__ uint32_t red[16];
   uint32_t m = 0;
   for (uint32_t i = threadIdx.x; i < nparts; i += blockDim.x) m = max(m, partial[i]);
   m = block_max_u32(m, red);
-  const float s = scale_from_amax(bf16_to_f32(m));
+  const float s = scale_from_amax<F>(bf16_to_f32(m));
   if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
-  quant_range(a, src, blockIdx.x * blockDim.x + threadIdx.x, a.total_units, gridDim.x * blockDim.x, s);
+  quant_range<F>(a, src, blockIdx.x * blockDim.x + threadIdx.x, a.total_units, gridDim.x * blockDim.x, s);
 }
 
+template <int F>
 __global__ __launch_bounds__(256) void quant_static_kernel(QuantArgs a, PlainSrc src, const float* scale) {
   const float s = *scale;
-  quant_range(a, src, blockIdx.x * blockDim.x + threadIdx.x, a.total_units, gridDim.x * blockDim.x, s);
+  quant_range<F>(a, src, blockIdx.x * blockDim.x + threadIdx.x, a.total_units, gridDim.x * blockDim.x, s);
 }
 
 // One workgroup per row: the row's own amax and scale, then its codes.
+template <int F>
 __global__ __launch_bounds__(256) void quant_per_row_kernel(QuantArgs a, PlainSrc src, float* scales_out) {
   __shared__ uint32_t red[16];
   const uint32_t r = blockIdx.x;
   const uint32_t u0 = r * a.units_per_row, u1 = u0 + a.units_per_row;
   uint32_t m = absmax_range(a, src, u0 + threadIdx.x, u1, blockDim.x);
   m = block_max_u32(m, red);
-  const float s = scale_from_amax(bf16_to_f32(m));
+  const float s = scale_from_amax<F>(bf16_to_f32(m));
   if (threadIdx.x == 0) scales_out[r] = s;
-  quant_range(a, src, u0 + threadIdx.x, u1, blockDim.x, s);
+  quant_range<F>(a, src, u0 + threadIdx.x, u1, blockDim.x, s);
 }
 
 // Residual add and RMS statistics, one workgroup per row: h' = bf16(h + d)
@@ -391,13 +394,13 @@ uint32_t grid_for_units(uint32_t units, uint32_t per_block, uint32_t cap) {
 
 // Dynamic per-tensor quantization of any source: one launch for small
 // tensors of cheap sources, else two (per-block maxima in the workspace).
-template <class Src>
+template <int F, class Src>
 hipError_t launch_dynamic(const QuantArgs& a, const Src& src, bool small_ok, float* scale_out, void* workspace,
                           hipStream_t stream) {
   if (small_ok && a.total_units <= kSmallUnits) {
     // one workgroup per 1024-unit slot: at most kSmallUnits / 1024 = 32
     const uint32_t grid = (a.total_units + kSmallThreads - 1) / kSmallThreads;
-    quant_dynamic_small_kernel<Src><<<grid, kSmallThreads, 0, stream>>>(a, src, scale_out);
+    quant_dynamic_small_kernel<F, Src><<<grid, kSmallThreads, 0, stream>>>(a, src, scale_out);
     return hipGetLastError();
   }
   uint32_t* partial = static_cast<uint32_t*>(workspace);
@@ -406,7 +409,7 @@ hipError_t launch_dynamic(const QuantArgs& a, const Src& src, bool small_ok, flo
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t grid2 = grid_for_units(a.total_units, 256 * kUnroll, 8192);
-  quant_from_partial_kernel<Src><<<grid2, 256, 0, stream>>>(a, src, partial, grid, scale_out);
+  quant_from_partial_kernel<F, Src><<<grid2, 256, 0, stream>>>(a, src, partial, grid, scale_out);
   return hipGetLastError();
 }
 
@@ -415,13 +418,15 @@ hipError_t launch_dynamic(const QuantArgs& a, const Src& src, bool small_ok, flo
 size_t quant_workspace_bytes() { return kPartialBlocks * sizeof(uint32_t); }
 
 // Shapes were validated by the caller: 0 <= rows, cols; rows*cols/8 < 2^31.
-hipError_t launch_quant_dynamic(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
+hipError_t launch_quant_dynamic(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int fmt, uint8_t* q,
                                 int64_t ld_q, float* scale_out, void* workspace, hipStream_t stream) {
   if (rows == 0 || cols == 0) {
     write_scale_kernel<<<1, 1, 0, stream>>>(scale_out, 1.0f);
     return hipGetLastError();
   }
-  return launch_dynamic(make_args(rows, cols, q, ld_q), plain_src(x, ld_x), true, scale_out, workspace, stream);
+  const QuantArgs a = make_args(rows, cols, q, ld_q);
+  if (fmt == kE5M2) return launch_dynamic<kE5M2>(a, plain_src(x, ld_x), true, scale_out, workspace, stream);
+  return launch_dynamic<kE4M3>(a, plain_src(x, ld_x), true, scale_out, workspace, stream);
 }
 
 size_t norm_quant_workspace_bytes(int64_t rows) {
@@ -446,7 +451,7 @@ hipError_t launch_add_rmsnorm_quant(const uint16_t* h, int64_t ld_h, const uint1
   const uint16_t* hs = delta ? h_out : h;
   const int64_t ld_hs = delta ? ld_h_out : ld_h;
   const NormSrc src{hs, ld_hs, inv_rms, y_out, ld_y, rows16(hs, ld_hs), y_out != nullptr && rows16(y_out, ld_y)};
-  return launch_dynamic(a, src, true, scale_out, workspace, stream);
+  return launch_dynamic<kE4M3>(a, src, true, scale_out, workspace, stream);
 }
 
 hipError_t launch_silu_mul_quant(const uint16_t* gu, int64_t ld_gu, int64_t rows, int64_t cols, uint16_t* y_out,
@@ -460,19 +465,22 @@ hipError_t launch_silu_mul_quant(const uint16_t* gu, int64_t ld_gu, int64_t rows
   const SiluMulSrc src{gu, ld_gu, y_out, ld_y, rows16(gu, ld_gu) && (cols % 8 == 0),
                        y_out != nullptr && rows16(y_out, ld_y)};
   // the activation is costly to evaluate: never the redundant one-launch path
-  return launch_dynamic(make_args(rows, cols, q, ld_q), src, false, scale_out, workspace, stream);
+  return launch_dynamic<kE4M3>(make_args(rows, cols, q, ld_q), src, false, scale_out, workspace, stream);
 }
 
-hipError_t launch_quant_static(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, const float* scale,
-                               uint8_t* q, int64_t ld_q, hipStream_t stream) {
+hipError_t launch_quant_static(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int fmt,
+                               const float* scale, uint8_t* q, int64_t ld_q, hipStream_t stream) {
   if (rows == 0 || cols == 0) return hipSuccess;
   QuantArgs a = make_args(rows, cols, q, ld_q);
-  quant_static_kernel<<<grid_for_units(a.total_units, 256 * kUnroll, 8192), 256, 0, stream>>>(a, plain_src(x, ld_x),
-                                                                                               scale);
+  const uint32_t grid = grid_for_units(a.total_units, 256 * kUnroll, 8192);
+  if (fmt == kE5M2)
+    quant_static_kernel<kE5M2><<<grid, 256, 0, stream>>>(a, plain_src(x, ld_x), scale);
+  else
+    quant_static_kernel<kE4M3><<<grid, 256, 0, stream>>>(a, plain_src(x, ld_x), scale);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_per_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
+hipError_t launch_quant_per_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int fmt, uint8_t* q,
                                 int64_t ld_q, float* scales_out, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   if (cols == 0) {
@@ -480,7 +488,10 @@ hipError_t launch_quant_per_row(const uint16_t* x, int64_t rows, int64_t cols, i
     return hipGetLastError();
   }
   QuantArgs a = make_args(rows, cols, q, ld_q);
-  quant_per_row_kernel<<<(uint32_t)rows, 256, 0, stream>>>(a, plain_src(x, ld_x), scales_out);
+  if (fmt == kE5M2)
+    quant_per_row_kernel<kE5M2><<<(uint32_t)rows, 256, 0, stream>>>(a, plain_src(x, ld_x), scales_out);
+  else
+    quant_per_row_kernel<kE4M3><<<(uint32_t)rows, 256, 0, stream>>>(a, plain_src(x, ld_x), scales_out);
   return hipGetLastError();
 }
 

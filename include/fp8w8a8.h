@@ -229,6 +229,34 @@ fp8_status fp8_silu_mul_quant_dynamic(const uint16_t* gu_bf16, int64_t ld_gu, in
                                       uint8_t* q_e4m3, int64_t ld_q, float* scale_out,
                                       void* workspace, void* stream);
 
+/*
+ * fp8 formats.  E4M3 is the pages' float8_e4m3fn (max 448) and the format of
+ * every call above.  E5M2 is OCP float8_e5m2 (max 57344; 2 mantissa bits,
+ * wider range), the extension the "Fp8 Quantization Support"
+ * (compressed-tensors PR 62) description names for the same quantization
+ * scheme.  The *_fmt calls below are the calls above with the format of
+ * each fp8 tensor as an argument: the same scale rule (amax / max of the
+ * format), division, round-to-nearest-even and saturation (to +-max);
+ * e5m2 infinities and NaNs are never produced from finite inputs.
+ */
+typedef enum { FP8_FORMAT_E4M3 = 0, FP8_FORMAT_E5M2 = 1 } fp8_format;
+
+fp8_status fp8_quant_dynamic_fmt(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                                 fp8_format fmt, uint8_t* q, int64_t ld_q, float* scale_out,
+                                 void* workspace, void* stream);
+fp8_status fp8_quant_static_fmt(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                                fp8_format fmt, const float* scale, uint8_t* q, int64_t ld_q,
+                                void* stream);
+fp8_status fp8_quant_dynamic_per_row_fmt(const uint16_t* x_bf16, int64_t rows, int64_t cols,
+                                         int64_t ld_x, fp8_format fmt, uint8_t* q, int64_t ld_q,
+                                         float* scales_out, void* stream);
+/* a_q holds fmt_a codes, w_q fmt_w codes (any mix); otherwise as fp8_scaled_mm. */
+fp8_status fp8_scaled_mm_fmt(const uint8_t* a_q, int64_t lda, fp8_format fmt_a,
+                             const uint8_t* w_q, int64_t ldw, fp8_format fmt_w,
+                             const float* s_a, const float* s_w, fp8_scale_mode mode,
+                             fp8_accum_mode accum, const uint16_t* bias_bf16, uint16_t* out_bf16,
+                             int64_t ldo, int64_t M, int64_t N, int64_t K, void* stream);
+
 /* Text describing the calling thread's most recent non-OK status. */
 const char* fp8_last_error(void);
 

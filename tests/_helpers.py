@@ -39,15 +39,16 @@ def bf16_to_f64(bits):
     return oracle.bf16_bits_to_f32(bits).astype(np.float64)
 
 
-def abs_dot(aq, sa, wq, sw, per_channel):
+def abs_dot(aq, sa, wq, sw, per_channel, fmt_a="e4m3", fmt_w="e4m3"):
     """sum_k |dec(a[m,k]) * dec(w[n,k])| * s_a * s_w[n] (fp64)."""
-    da = np.abs(oracle.decode(aq)); dw = np.abs(oracle.decode(wq))
+    da = np.abs(oracle.FORMATS[fmt_a][0](aq)); dw = np.abs(oracle.FORMATS[fmt_w][0](wq))
     s = np.asarray(sw, np.float32).astype(np.float64)
     col = s if per_channel else np.full(wq.shape[0], s[0])
     return (da @ dw.T) * float(sa) * col[None, :]
 
 
-def assert_gemm_close(out_bits, ref, aq, sa, wq, sw, per_channel, rows=None, bias_bits=None, accum="fp32"):
+def assert_gemm_close(out_bits, ref, aq, sa, wq, sw, per_channel, rows=None, bias_bits=None, accum="fp32",
+                      fmt_a="e4m3", fmt_w="e4m3"):
     """Check bf16 GPU output against the exact oracle output, element-wise.
 
     rows: the output rows that `ref` covers (ref has len(rows) rows).
@@ -60,8 +61,8 @@ def assert_gemm_close(out_bits, ref, aq, sa, wq, sw, per_channel, rows=None, bia
     """
     out = bf16_to_f64(out_bits if rows is None else out_bits[rows])
     a_sub = aq if rows is None else aq[rows]
-    an = oracle.dequant_row_norms(a_sub, [sa], per_row=False)
-    wn = oracle.dequant_row_norms(wq, sw, per_row=per_channel)
+    an = oracle.dequant_row_norms(a_sub, [sa], per_row=False, fmt=fmt_a)
+    wn = oracle.dequant_row_norms(wq, sw, per_row=per_channel, fmt=fmt_w)
     err = np.abs(out - ref)
     bound = ABS_NORM * np.outer(an, wn)
     if bias_bits is not None:
@@ -69,7 +70,7 @@ def assert_gemm_close(out_bits, ref, aq, sa, wq, sw, per_channel, rows=None, bia
     bad = err > bound
     assert not bad.any(), f"{bad.sum()} elements over the norm bound; worst err/bound {np.max(err / np.maximum(bound, 1e-300)):.3g}"
     if accum == "fp8":
-        ad = abs_dot(a_sub, sa, wq, sw, per_channel)
+        ad = abs_dot(a_sub, sa, wq, sw, per_channel, fmt_a, fmt_w)
         lim = 2.0 ** -8 * ad + 2.0 ** -8 * np.abs(ref)
         over = err > lim
         assert not over.any(), f"{over.sum()} elements over the fp8-accumulation bound"

@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "fp8_quant_workspace_bytes", "fp8_quant_dynamic", "fp8_quant_static",
         "fp8_quant_dynamic_per_row", "fp8_scaled_mm", "fp8_last_error",
-        "fp8_norm_quant_workspace_bytes", "fp8_add_rmsnorm_quant_dynamic", "fp8_silu_mul_quant_dynamic"])
+        "fp8_norm_quant_workspace_bytes", "fp8_add_rmsnorm_quant_dynamic", "fp8_silu_mul_quant_dynamic",
+        "fp8_quant_dynamic_fmt", "fp8_quant_static_fmt", "fp8_quant_dynamic_per_row_fmt", "fp8_scaled_mm_fmt"])
 
 
 def test_library_exports_every_declared_function(lib):
@@ -121,3 +122,14 @@ def test_fused_producers_reject_bad_arguments(lib):
     assert g(P, 16, 2, 8, NULL, 0, P, 8, P, NULL, NULL) == INVALID  # null workspace
     assert g(P, 16, -2, 8, NULL, 0, P, 8, P, P, NULL) == INVALID
     assert lib.fp8_norm_quant_workspace_bytes(16384) >= lib.fp8_quant_workspace_bytes() + 8 * 16384
+
+
+def test_format_arguments_are_validated(lib):
+    assert lib.fp8_quant_dynamic_fmt(P, 2, 4, 4, 2, P, 4, P, P, NULL) == INVALID
+    assert "format" in _err(lib)
+    assert lib.fp8_quant_static_fmt(P, 2, 4, 4, -1, P, P, 4, NULL) == INVALID
+    assert lib.fp8_quant_dynamic_per_row_fmt(P, 2, 4, 4, 7, P, 4, P, NULL) == INVALID
+    f = lib.fp8_scaled_mm_fmt
+    assert f(P, 64, 0, P, 64, 3, P, P, 0, 0, NULL, P, 32, 4, 32, 64, NULL) == INVALID
+    assert f(P, 64, 5, P, 64, 1, P, P, 0, 0, NULL, P, 32, 4, 32, 64, NULL) == INVALID
+    assert f(P, 63, 1, P, 64, 1, P, P, 0, 0, NULL, P, 32, 4, 32, 64, NULL) == INVALID   # lda < K
