@@ -22,6 +22,13 @@
 //     double-buffered (2 x 64 KiB).  Out-of-range lanes (rows past M or N,
 //     k past K) return zeros through the buffer range check, so edge tiles
 //     need no branches and k tails add nothing.
+//   * Issue order within a k step (pinned with scheduling barriers): the
+//     first half's fragments, then the first half's 16 products with one
+//     block of the next step's loads and two of the second half's fragment
+//     reads after each pair, then the second half's products.  Issued in one
+//     burst, the 16 load instructions of a wave stall its instruction stream
+//     on the texture unit while the matrix pipe idles (measured: ~30% of
+//     the step even with every load hitting L2).
 //   * LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at
 //     position c ^ (r & 7) ^ ((r >> 3) & 1), so the rows that consecutive
 //     lanes read land in different bank groups.
@@ -170,21 +177,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
   // the chunk (hence k offset) a lane fetches depends only on its row within
   // the block and on the block's parity
   const int dchunk_k0 = (dphys ^ drow_in_blk) * 16, dchunk_k1 = (dphys ^ drow_in_blk ^ 1) * 16;
-  auto dma = [&](int stage, const Tile& t, int k0, bool step_valid) {
-    const bool kin0 = step_valid && k0 + dchunk_k0 < g.K, kin1 = step_valid && k0 + dchunk_k1 < g.K;
+  // one block of each operand (2 instructions); dma() issues all 8 blocks
+  auto dma_part = [&](int stage, const Tile& t, int k0, bool step_valid, int i) {
+    const bool kin = step_valid && k0 + ((i & 1) ? dchunk_k1 : dchunk_k0) < g.K;
     uint8_t* As = smem + stage * kStageBytes;
     uint8_t* Ws = As + kOperandBytes;
+    const int blk = __builtin_amdgcn_readfirstlane(wave * 8 + i);
+    const uint32_t oa = kin ? dvoff_a[i] + k0 : kOutOfRange;
+    const uint32_t ow = kin ? dvoff_w[i] + k0 : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(t.ra, (__attribute__((address_space(3))) void*)(As + blk * 1024), 16,
+                                             (int)oa, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(t.rw, (__attribute__((address_space(3))) void*)(Ws + blk * 1024), 16,
+                                             (int)ow, 0, 0, 0);
+  };
+  auto dma = [&](int stage, const Tile& t, int k0, bool step_valid) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int blk = __builtin_amdgcn_readfirstlane(wave * 8 + i);
-      const bool kin = (i & 1) ? kin1 : kin0;
-      const uint32_t oa = kin ? dvoff_a[i] + k0 : kOutOfRange;
-      const uint32_t ow = kin ? dvoff_w[i] + k0 : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(t.ra, (__attribute__((address_space(3))) void*)(As + blk * 1024), 16,
-                                               (int)oa, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(t.rw, (__attribute__((address_space(3))) void*)(Ws + blk * 1024), 16,
-                                               (int)ow, 0, 0, 0);
-    }
+    for (int i = 0; i < 8; ++i) dma_part(stage, t, k0, step_valid, i);
   };
 
   const int KT = (g.K + BK - 1) / BK;
@@ -252,31 +260,48 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
       const uint8_t* Ws = As + kOperandBytes;
       // next step's loads into the idle buffer: this tile's next step, or the
       // next tile's first step (zeros after the last tile)
-      if (kt + 1 < KT)
-        dma((step + 1) & 1, cur, (kt + 1) * BK, true);
-      else
-        dma((step + 1) & 1, nxt, 0, has_next);
+      const bool last_step = kt + 1 >= KT;
+      Tile tgt;
+      tgt.ra = last_step ? nxt.ra : cur.ra;
+      tgt.rw = last_step ? nxt.rw : cur.rw;
+      const int k_next = last_step ? 0 : (kt + 1) * BK;
+      const bool v_next = last_step ? has_next : true;
+      const int nstage = (step + 1) & 1;
+      // order: the first half's fragments; then the first half's 16 products,
+      // each pair followed by one block of next-step loads and two of the
+      // second half's fragment reads; then the second half's products
       v8i wf[2][4], af[2][4];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int i = 0; i < 4; ++i) wf[0][i] = read_frag(Ws, wn * 128 + i * 32 + frow, fchunk);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wf[ks][i] = read_frag(Ws, wn * 128 + i * 32 + frow, ks * 4 + fchunk);
+      for (int j = 0; j < 4; ++j) af[0][j] = read_frag(As, wm * 128 + j * 32 + frow, fchunk);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!EXACT) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) af[ks][j] = read_frag(As, wm * 128 + j * 32 + frow, ks * 4 + fchunk);
-      }
+        for (int p = 0; p < 8; ++p) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if constexpr (!EXACT) {
+          for (int q = 0; q < 2; ++q) {
+            const int i = (2 * p + q) >> 2, j = (2 * p + q) & 3;
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[0][i], af[0][j], acc[i][j], FW, FA,
+                                                                         0, 0, 0, 0);
+          }
+          dma_part(nstage, tgt, k_next, v_next, p);
+          if (p < 4) wf[1][p] = read_frag(Ws, wn * 128 + p * 32 + frow, 4 + fchunk);
+          else af[1][p - 4] = read_frag(As, wm * 128 + (p - 4) * 32 + frow, 4 + fchunk);
+          __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              // operand formats: cbsz for the A operand (W), blgp for B (A_q); 0 = fp8, 1 = bf8
-              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[ks][i], af[ks][j], acc[i][j], FW, FA,
-                                                                           0, 0, 0, 0);
-        } else {
-          // the lane's 32 k-values in four slices of 8 (same slicing for
-          // both operands), one bf16 32x32x16 product per slice
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[1][i], af[1][j], acc[i][j], FW, FA,
+                                                                         0, 0, 0, 0);
+      } else {
+        // the lane's 32 k-values in four slices of 8 (same slicing for
+        // both operands), one bf16 32x32x16 product per slice; two blocks of
+        // loads and two fragment reads after each slice of the first half
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             bf16x8 wb[4], ab[4];
@@ -289,6 +314,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
 #pragma unroll
               for (int j = 0; j < 4; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb[i], ab[j], acc[i][j], 0, 0, 0);
+            if (ks == 0) {
+              dma_part(nstage, tgt, k_next, v_next, 2 * t);
+              dma_part(nstage, tgt, k_next, v_next, 2 * t + 1);
+              wf[1][t] = read_frag(Ws, wn * 128 + t * 32 + frow, 4 + fchunk);
+              af[1][t] = read_frag(As, wm * 128 + t * 32 + frow, 4 + fchunk);
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
         }
       }
