@@ -4,11 +4,13 @@
 // quantization", opening post: activations are quantized per call): the
 // scale is amax/448, so amax needs the whole tensor before any code can be
 // written.
-//   * Small tensors (decode activations, up to 256 Ki elements): one launch
-//     of up to 32 workgroups.  Every workgroup reduces the whole tensor
-//     itself (at most 512 KiB, served by L2 after the first touch), so no
+//   * Small tensors (decode activations, up to 128 Ki elements): one launch
+//     of up to 16 workgroups.  Every workgroup reduces the whole tensor
+//     itself (at most 256 KiB, served by L2 after the first touch), so no
 //     workgroup waits for another, and quantizes only its own share, which
-//     it kept in registers from that pass.
+//     it kept in registers from that pass.  (Past that size the redundant
+//     reads cost more than a second launch: measured 11.5 us against 6.8 us
+//     for 16 x 14336.)
 //   * Large tensors (prefill): two launches on the same stream -- per-block
 //     maxima into the workspace, then every block folds those maxima (a few
 //     KiB, from L2) into the scale and quantizes its share.
@@ -234,7 +236,7 @@ __device__ __forceinline__ void quant_range(const QuantArgs& a, const Src& src, 
 // threads, 8 loads of 16 bytes in flight each), keeping in registers the
 // slot it will quantize -- units blockIdx.x * 1024 + threadIdx.x -- so the
 // codes need no second read.  The grid has one workgroup per slot (at most
-// 32); workgroup 0 writes the scale.  Only for cheap sources: every
+// 16); workgroup 0 writes the scale.  Only for cheap sources: every
 // workgroup evaluates the source over the whole tensor.
 constexpr int kSmallThreads = 1024;
 constexpr int kSmallBatch = 8;
@@ -385,7 +387,7 @@ bool rows16(const void* p, int64_t ld) { return ((uintptr_t)p % 16 == 0) && (ld 
 PlainSrc plain_src(const uint16_t* x, int64_t ld_x) { return PlainSrc{x, ld_x, rows16(x, ld_x)}; }
 
 constexpr uint32_t kPartialBlocks = 1024;         // max blocks of the two-launch path
-constexpr uint32_t kSmallUnits = 1u << 15;        // <= 256 Ki elements (512 KiB): one launch
+constexpr uint32_t kSmallUnits = 1u << 14;        // <= 128 Ki elements (256 KiB): one launch
 
 uint32_t grid_for_units(uint32_t units, uint32_t per_block, uint32_t cap) {
   uint32_t g = (units + per_block - 1) / per_block;
@@ -398,7 +400,7 @@ template <int F, class Src>
 hipError_t launch_dynamic(const QuantArgs& a, const Src& src, bool small_ok, float* scale_out, void* workspace,
                           hipStream_t stream) {
   if (small_ok && a.total_units <= kSmallUnits) {
-    // one workgroup per 1024-unit slot: at most kSmallUnits / 1024 = 32
+    // one workgroup per 1024-unit slot: at most kSmallUnits / 1024 = 16
     const uint32_t grid = (a.total_units + kSmallThreads - 1) / kSmallThreads;
     quant_dynamic_small_kernel<F, Src><<<grid, kSmallThreads, 0, stream>>>(a, src, scale_out);
     return hipGetLastError();
