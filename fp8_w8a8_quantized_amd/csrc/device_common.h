@@ -29,6 +29,17 @@ __device__ __forceinline__ constexpr float fmt_max() {
 constexpr int kWaitLgkm0 = 0xC07F;
 // s_waitcnt immediate for gfx9: vmcnt(0), expcnt and lgkmcnt left at max.
 constexpr int kWaitVm0 = 0x0F70;
+// s_waitcnt immediate for gfx9: vmcnt(n), 0 <= n < 64 (vmcnt bits 3:0 and
+// 15:14), expcnt and lgkmcnt left at max.
+constexpr int wait_vmcnt(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }
+static_assert(wait_vmcnt(0) == kWaitVm0 && wait_vmcnt(32) == 0x8F70, "s_waitcnt vmcnt encoding");
+
+// Raw buffer resources (gfx9): word 3 selects the 32-bit data format.  A
+// load whose byte offset reaches num_records returns zeros without touching
+// memory; offsets at or above kOutOfRange are out of range for every
+// resource these kernels build (num_records stays below 2^31).
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr uint32_t kOutOfRange = 0x80000000u;
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);

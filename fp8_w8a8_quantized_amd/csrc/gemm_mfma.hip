@@ -68,8 +68,6 @@ constexpr int kOperandBytes = BM * BK;  // 32 KiB per operand per stage
 constexpr int kStageBytes = 2 * kOperandBytes;
 constexpr int kGroupM = 8;
 constexpr int kEpiParamBytes = BN * 4 + BN * 2;
-constexpr uint32_t kOutOfRange = 0x80000000u;
-constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9)
 // Epilogue: 32 rows per round, 4 rounds, 8 store instructions per round.
 constexpr int kEpiStores = 32;
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in

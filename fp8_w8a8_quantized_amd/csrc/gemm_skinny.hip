@@ -107,34 +107,46 @@ __device__ __forceinline__ v4f mfma_fp8_as_bf16(v8i wf, v8i af, v4f acc) {
   return acc;
 }
 
-// Sum the waves' partial tiles through LDS in wave order and apply the
-// rescale epilogue.  acc holds D[n][m] for n = n0 + 4 * (lane / 16) + i and
-// m = m0 + lane % 16.
 // The epilogue's per-column factors, loaded at kernel start so that their
-// memory latency overlaps the main loop instead of following it.
+// memory latency overlaps the main loop instead of following it.  They are
+// kept as loaded (no arithmetic on them until the epilogue), so no wait for
+// them lands before the main loop.
 struct EpiParams {
-  float sc[4], bs[4];
+  float sw[4];
+  uint32_t bias[4];
 };
 
 __device__ __forceinline__ EpiParams load_epi_params(const GemmArgs& g, int lane, int n0) {
+  // Buffer loads based at the block's first column (offsets below 64 bytes
+  // whatever N is); a missing bias is a resource of size 0, whose loads
+  // return zeros.  No load sits under a branch.
+  const int cols = min(g.N - n0, 16);
+  const __amdgpu_buffer_rsrc_t rsw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.per_channel ? g.s_w + n0 : g.s_w), (short)0, g.per_channel ? 4 * cols : 4, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rbias = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.bias ? g.bias + n0 : reinterpret_cast<const uint16_t*>(g.s_w)), (short)0, g.bias ? 2 * cols : 0,
+      kRsrcWord3);
   EpiParams p;
-  const float sa = *g.s_a;
-  const int nb = n0 + 4 * (lane >> 4);
+  const int cb = 4 * (lane >> 4);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int n = min(nb + i, g.N - 1);
-    p.sc[i] = sa * (g.per_channel ? g.s_w[n] : g.s_w[0]);
-    p.bs[i] = g.bias ? bf16_to_f32(g.bias[n]) : 0.0f;
+    const int c = min(cb + i, cols - 1);
+    p.sw[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsw, g.per_channel ? 4 * c : 0, 0, 0));
+    p.bias[i] = __builtin_amdgcn_raw_buffer_load_b16(rbias, 2 * c, 0, 0);
   }
   return p;
 }
 
+// Sum the waves' partial tiles through LDS in wave order and apply the
+// rescale epilogue.  acc holds D[n][m] for n = n0 + 4 * (lane / 16) + i and
+// m = m0 + lane % 16.
 __device__ __forceinline__ void reduce_and_store(const GemmArgs& g, v4f acc, float (*red)[4][64], int nw,
                                                  int wave, int lane, int n0, int m0, const EpiParams& ep) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) red[wave][i][lane] = acc[i];
   __syncthreads();
   if (wave != 0) return;
+  const float sa = *g.s_a;
   float sum[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -148,7 +160,8 @@ __device__ __forceinline__ void reduce_and_store(const GemmArgs& g, v4f acc, flo
   const int nb = n0 + 4 * grp;
   uint32_t o[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16_rne(__builtin_fmaf(sum[i], ep.sc[i], ep.bs[i]));
+  for (int i = 0; i < 4; ++i)
+    o[i] = f32_to_bf16_rne(__builtin_fmaf(sum[i], sa * ep.sw[i], bf16_to_f32(ep.bias[i])));
   uint16_t* orow = g.out + (int64_t)m * g.ldo;
   if (nb + 3 < g.N && ((uintptr_t)(orow + nb) % 8) == 0) {
     uint2 v;
@@ -169,22 +182,30 @@ __device__ __forceinline__ v8i cat8(v4i lo, v4i hi) {
   return f;
 }
 
-// Aligned layouts: rows 16-byte aligned and K % 16 == 0, so every 16-byte
-// chunk lies wholly inside or wholly outside [0, K).
-// Launched with blockDim.x = 64 * nw (nw <= kMaxWaves) and
-// skinny_lds_bytes(nw) bytes of dynamic LDS: per wave a 2 x 4 KiB staging
-// buffer, then the nw x 1 KiB reduction area.
-constexpr int kMaxWaves = 8;
-constexpr int kStageBytesPerWave = 2 * 16 * 256;
+// Aligned layouts: rows 16-byte aligned, K % 16 == 0 and pitches below
+// 2^27 bytes, so every 16-byte chunk lies wholly inside or wholly outside
+// [0, K) and a 16-row block spans less than 2^31 bytes.
+constexpr int64_t kMaxPitch = int64_t(1) << 27;
+// Waves per workgroup and steps in flight per wave, measured on the decode
+// shapes of an 8B-class model (K = 4096 and 14336): deeper pipelines (3-8
+// steps) and 8 or 16 waves were slower, a single step in flight about as
+// fast for the shapes with one workgroup per CU.
+constexpr int kSkinnyWaves = 4;
+constexpr int kSkinnyDepth = 2;
 
-inline size_t skinny_lds_bytes(int nw) { return (size_t)nw * (kStageBytesPerWave + 4 * 64 * sizeof(float)); }
-
-template <int P, int FA, int FW>
-__global__ __launch_bounds__(kMaxWaves * 64) void gemm_skinny_kernel(GemmArgs g) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
-  const int NW = blockDim.x >> 6;
-  uint8_t (*stage)[2][16 * 256] = reinterpret_cast<uint8_t (*)[2][16 * 256]>(dyn_lds);
-  float (*red)[4][64] = reinterpret_cast<float (*)[4][64]>(dyn_lds + NW * kStageBytesPerWave);
+// Rolling pipeline of depth D: before a wave transposes and multiplies step
+// s it issues the loads of step s + D - 1, so D - 1 steps stay in flight
+// while it computes.  Every load is an unconditional buffer load: rows past
+// N or M, chunks past K and steps past the wave's range get an offset past
+// the resource's end and return zeros without a memory access.  With no
+// load under a branch the compiler's wait counts are exact (vmcnt of the
+// steps still in flight), never a full drain.
+// LDS: per wave a 2 x 4 KiB staging buffer (weight and activation step),
+// then the NW x 1 KiB reduction area.
+template <int NW, int D, int FA, int FW>
+__global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage[NW][2][16 * 256];
+  __shared__ float red[NW][4][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r = lane & 15, grp = lane >> 4;
@@ -194,59 +215,82 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemm_skinny_kernel(GemmArgs g)
   const int s_begin = min(wave * per, steps), s_end = min(s_begin + per, steps);
   // load mapping: instruction j covers rows 4j + lane/16, bytes 16 * (lane % 16)
   const int lr = lane >> 4, lc = (lane & 15) * 16;
-  const uint8_t* wp[4];
-  const uint8_t* ap[4];
-  bool wok[4], aok[4];
+  const int rows_w = min(g.N - n0, 16), rows_a = min(g.M - m0, 16);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.w + (int64_t)n0 * g.ldw), (short)0, (int)(rows_w * g.ldw), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.a + (int64_t)m0 * g.lda), (short)0, (int)(rows_a * g.lda), kRsrcWord3);
+  // 32-bit offsets (pitches are below 2^27)
+  const uint32_t ldw = (uint32_t)g.ldw, lda = (uint32_t)g.lda;
+  uint32_t wo[4], ao[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int n = n0 + 4 * j + lr, m = m0 + 4 * j + lr;
-    wok[j] = n < g.N;
-    aok[j] = m < g.M;
-    wp[j] = g.w + (int64_t)(wok[j] ? n : 0) * g.ldw + lc;
-    ap[j] = g.a + (int64_t)(aok[j] ? m : 0) * g.lda + lc;
+    const uint32_t row = 4 * j + lr;
+    wo[j] = (int)row < rows_w ? row * ldw + lc : kOutOfRange;
+    ao[j] = (int)row < rows_a ? row * lda + lc : kOutOfRange;
   }
   uint8_t* LW = stage[wave][0];
   uint8_t* LA = stage[wave][1];
   const int swz_w = (lane & 15);  // chunk written by this lane (before the XOR)
 
-  const EpiParams ep = load_epi_params(g, lane, n0);
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = s_begin; s < s_end; s += P) {
-    v4i wv[P][4], av[P][4];
+  v4i wv[D][4], av[D][4];
+  auto issue = [&](int slot, int s) {
+    const int k0 = s * 256;
+    const bool kin = s < s_end && k0 + lc < g.K;
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      const int k0 = (s + p) * 256;
-      const bool kin = s + p < s_end && k0 + lc < g.K;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        wv[p][j] = (kin && wok[j]) ? *reinterpret_cast<const v4i*>(wp[j] + k0) : v4i{0, 0, 0, 0};
-        av[p][j] = (kin && aok[j]) ? *reinterpret_cast<const v4i*>(ap[j] + k0) : v4i{0, 0, 0, 0};
-      }
+    for (int j = 0; j < 4; ++j) {
+      wv[slot][j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rw, kin ? wo[j] + k0 : kOutOfRange, 0, 0));
+      av[slot][j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                                                ra, kin ? ao[j] + k0 : kOutOfRange, 0, 0));
     }
+  };
+  // Issue order is pinned: the epilogue's factors first (the oldest loads,
+  // so waiting for any step covers them), then the steps in order.  After
+  // each issue an explicit wait leaves exactly the D - 1 younger steps in
+  // flight, on every path (the compiler's own waits would otherwise follow
+  // the worst order it can prove, which drains the pipeline).
+  // (the offset arithmetic above stays before every load: a 64-bit
+  // multiply-add it may use reads a don't-care register that could alias a
+  // pending load's destination and force a drain)
+  __builtin_amdgcn_sched_barrier(0);
+  const EpiParams ep = load_epi_params(g, lane, n0);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      if (s + p >= s_end) break;
+  for (int d = 0; d < D - 1; ++d) {
+    issue(d, s_begin + d);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = s_begin; s < s_end; s += D) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = 4 * j + lr;
-        *reinterpret_cast<v4i*>(LW + row * 256 + ((swz_w ^ row) << 4)) = wv[p][j];
-        *reinterpret_cast<v4i*>(LA + row * 256 + ((swz_w ^ row) << 4)) = av[p][j];
+    for (int d = 0; d < D; ++d) {
+      issue((d + D - 1) % D, s + d + D - 1);
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(8 * (D - 1)));
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + d < s_end) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = 4 * j + lr;
+          *reinterpret_cast<v4i*>(LW + row * 256 + ((swz_w ^ row) << 4)) = wv[d][j];
+          *reinterpret_cast<v4i*>(LA + row * 256 + ((swz_w ^ row) << 4)) = av[d][j];
+        }
+        // the same wave reads what its other lanes wrote: LDS operations of a
+        // wave complete in order, so waiting for them suffices
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int c0 = t * 8 + grp, c1 = t * 8 + 4 + grp;
+          const v4i wlo = *reinterpret_cast<const v4i*>(LW + r * 256 + ((c0 ^ r) << 4));
+          const v4i whi = *reinterpret_cast<const v4i*>(LW + r * 256 + ((c1 ^ r) << 4));
+          const v4i alo = *reinterpret_cast<const v4i*>(LA + r * 256 + ((c0 ^ r) << 4));
+          const v4i ahi = *reinterpret_cast<const v4i*>(LA + r * 256 + ((c1 ^ r) << 4));
+          acc = mfma_fp8_as_bf16<FA, FW>(cat8(wlo, whi), cat8(alo, ahi), acc);
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_wave_barrier();
       }
-      // the same wave reads what its other lanes wrote: LDS operations of a
-      // wave complete in order, so waiting for them suffices
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int c0 = t * 8 + grp, c1 = t * 8 + 4 + grp;
-        const v4i wlo = *reinterpret_cast<const v4i*>(LW + r * 256 + ((c0 ^ r) << 4));
-        const v4i whi = *reinterpret_cast<const v4i*>(LW + r * 256 + ((c1 ^ r) << 4));
-        const v4i alo = *reinterpret_cast<const v4i*>(LA + r * 256 + ((c0 ^ r) << 4));
-        const v4i ahi = *reinterpret_cast<const v4i*>(LA + r * 256 + ((c1 ^ r) << 4));
-        acc = mfma_fp8_as_bf16<FA, FW>(cat8(wlo, whi), cat8(alo, ahi), acc);
-      }
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      __builtin_amdgcn_wave_barrier();
     }
   }
   reduce_and_store(g, acc, red, NW, wave, lane, n0, m0, ep);
@@ -291,18 +335,12 @@ hipError_t launch_generic(const GemmArgs& g, dim3 grid, hipStream_t stream) {
 template <int FA, int FW>
 hipError_t launch_skinny(const GemmArgs& g, hipStream_t stream) {
   const bool aligned = ((uintptr_t)g.a % 16 == 0) && ((uintptr_t)g.w % 16 == 0) && (g.lda % 16 == 0) &&
-                       (g.ldw % 16 == 0) && (g.K % 16 == 0);
+                       (g.ldw % 16 == 0) && (g.K % 16 == 0) && g.lda < kMaxPitch && g.ldw < kMaxPitch &&
+                       g.N < (1 << 29);
   const int64_t tiles_n = (g.N + 15) / 16, tiles_m = (g.M + 15) / 16;
   dim3 grid((unsigned)tiles_n, (unsigned)tiles_m);
   if (aligned) {
-    // 8 waves for long K (more bytes in flight per workgroup), else 4
-    // dynamic LDS above 64 KiB must be allowed once per process
-    static const hipError_t lds_attr = hipFuncSetAttribute(
-        (const void*)gemm_skinny_kernel<2, FA, FW>, hipFuncAttributeMaxDynamicSharedMemorySize,
-        (int)skinny_lds_bytes(kMaxWaves));
-    if (lds_attr != hipSuccess) return lds_attr;
-    const int nw = (g.K + 255) / 256 >= 32 ? 8 : 4;
-    gemm_skinny_kernel<2, FA, FW><<<grid, nw * 64, skinny_lds_bytes(nw), stream>>>(g);
+    gemm_skinny_kernel<kSkinnyWaves, kSkinnyDepth, FA, FW><<<grid, kSkinnyWaves * 64, 0, stream>>>(g);
     return hipGetLastError();
   }
   const int64_t tiles = tiles_n * tiles_m;
