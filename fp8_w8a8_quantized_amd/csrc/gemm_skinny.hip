@@ -202,7 +202,11 @@ constexpr int kSkinnyDepth = 2;
 // steps still in flight), never a full drain.
 // LDS: per wave a 2 x 4 KiB staging buffer (weight and activation step),
 // then the NW x 1 KiB reduction area.
-template <int NW, int D, bool IL, int FA, int FW>
+// Cache-policy bits of a buffer load (gfx950): nt, a non-temporal (streaming)
+// access.
+constexpr int kNonTemporal = 2;
+
+template <int NW, int D, bool IL, bool NT, int FA, int FW>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[NW][2][16 * 256];
   __shared__ float red[NW][4][64];
@@ -252,7 +256,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       wv[slot][j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
-                                                rw, kin ? wo[j] + k0 : kOutOfRange, 0, 0));
+                                                rw, kin ? wo[j] + k0 : kOutOfRange, 0, NT ? kNonTemporal : 0));
       av[slot][j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
                                                 ra, kin ? ao[j] + k0 : kOutOfRange, 0, 0));
     }
@@ -352,12 +356,23 @@ hipError_t launch_skinny(const GemmArgs& g, hipStream_t stream) {
   const int64_t tiles_n = (g.N + 15) / 16, tiles_m = (g.M + 15) / 16;
   dim3 grid((unsigned)tiles_n, (unsigned)tiles_m);
   if (aligned) {
-    // interleaved steps for long K (>= 8192), contiguous ranges otherwise:
-    // each the faster on the decode shapes (K = 14336 and K = 4096)
-    if ((g.K + 255) / 256 >= 32)
-      gemm_skinny_kernel<kSkinnyWaves, kSkinnyDepth, true, FA, FW><<<grid, kSkinnyWaves * 64, 0, stream>>>(g);
+    // Interleaved steps for long K (>= 8192), contiguous ranges otherwise;
+    // weights of 32 MiB and more streamed with non-temporal loads.  Each
+    // choice was the faster one on the decode shapes of an 8B-class model
+    // with weights streaming from HBM: the non-temporal hint took gate_up
+    // (112 MiB) from 25.9 to 23.2 us and down (56 MiB) from 14.0 to 13.4 us,
+    // but slowed QKV (24 MiB) and O (16 MiB) by 0.4-1 us.
+    const bool il = (g.K + 255) / 256 >= 32;
+    const bool nt = (int64_t)g.N * g.K >= (int64_t(32) << 20);
+    const dim3 block(kSkinnyWaves * 64);
+    if (il && nt)
+      gemm_skinny_kernel<kSkinnyWaves, kSkinnyDepth, true, true, FA, FW><<<grid, block, 0, stream>>>(g);
+    else if (il)
+      gemm_skinny_kernel<kSkinnyWaves, kSkinnyDepth, true, false, FA, FW><<<grid, block, 0, stream>>>(g);
+    else if (nt)
+      gemm_skinny_kernel<kSkinnyWaves, kSkinnyDepth, false, true, FA, FW><<<grid, block, 0, stream>>>(g);
     else
-      gemm_skinny_kernel<kSkinnyWaves, kSkinnyDepth, false, FA, FW><<<grid, kSkinnyWaves * 64, 0, stream>>>(g);
+      gemm_skinny_kernel<kSkinnyWaves, kSkinnyDepth, false, false, FA, FW><<<grid, block, 0, stream>>>(g);
     return hipGetLastError();
   }
   const int64_t tiles = tiles_n * tiles_m;
