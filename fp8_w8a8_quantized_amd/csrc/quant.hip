@@ -96,15 +96,16 @@ __device__ __forceinline__ float bf16_at(v4i v, int i) {
 }
 
 // float64 -> bf16 bits, one round-to-nearest-even (no double rounding through
-// float32): the value is rounded to a multiple of its bf16 step 2^max(e-8,
-// -133), where 2^(e-1) <= |x| < 2^e; the result is a bf16 value, exact in
-// float32.  Finite inputs (NaN stays NaN).
+// float32): the value is rounded to a multiple of its bf16 step 2^k,
+// k = max(e-8, -133), where 2^(e-1) <= |x| < 2^e; the result is a bf16 value,
+// exact in float32.  The scalings by 2^-k and 2^k are exact (x * 2^-k has at
+// most 8 integer bits), so no division is needed.  NaN stays NaN.
 __device__ __forceinline__ uint32_t f64_to_bf16_rne(double x) {
   if (x != x) return 0x7fc0u;
   int e;
   (void)frexp(x, &e);
-  const double step = ldexp(1.0, max(e - 8, -133));
-  const double r = rint(x / step) * step;
+  const int k = max(e - 8, -133);
+  const double r = ldexp(rint(ldexp(x, -k)), k);
   return __float_as_uint((float)r) >> 16;
 }
 
@@ -128,7 +129,11 @@ __device__ __forceinline__ v4i pack8_bf16(const float f[8]) {
 // unit's codes.
 
 // The activations themselves.
+// kUnitsPerThread: the units a thread handles in the two-launch path (cheap
+// sources take several to keep loads in flight; costly ones one, to spread
+// the arithmetic over the whole chip).
 struct PlainSrc {
+  static constexpr uint32_t kUnitsPerThread = 4;
   const uint16_t* x;
   int64_t ld;
   bool vec;  // 16-byte aligned rows
@@ -139,8 +144,9 @@ struct PlainSrc {
 };
 
 // Unit-weight RMS normalization: y = bf16(h * inv_rms[row]) in float64,
-// inv_rms from row_stats_kernel.
+// inv_rms from norm_rows_kernel.
 struct NormSrc {
+  static constexpr uint32_t kUnitsPerThread = 1;
   const uint16_t* h;
   int64_t ld_h;
   const double* inv_rms;
@@ -163,6 +169,7 @@ struct NormSrc {
 // Gated activation, gate half first: y = bf16(silu(g) * u) with
 // silu(g) = g / (1 + exp(-g)), in float64.
 struct SiluMulSrc {
+  static constexpr uint32_t kUnitsPerThread = 1;
   const uint16_t* gu;  // row r: gate columns [0, cols), up columns [cols, 2 cols)
   int64_t ld;
   uint16_t* y;  // optional copy of the activated values
@@ -320,48 +327,66 @@ __global__ __launch_bounds__(256) void quant_per_row_kernel(QuantArgs a, PlainSr
   quant_range<F>(a, src, u0 + threadIdx.x, u1, blockDim.x, s);
 }
 
-// Residual add and RMS statistics, one workgroup per row: h' = bf16(h + d)
+// Residual add, RMS statistics and the absmax of the normalized values, for
+// rows b, b + gridDim.x, ... of workgroup b.  Per row: h' = bf16(h + d)
 // (float32 add, one rounding; written to h_out when d is given), then
-// inv_rms[row] = 1 / sqrt(sum(h'^2) / cols + eps) in float64.  The sum runs
-// in a fixed order (per-thread units in order, then a fixed butterfly and
-// wave order), so it is deterministic.
-__global__ __launch_bounds__(256) void row_stats_kernel(const uint16_t* h, int64_t ld_h, const uint16_t* d,
-                                                        int64_t ld_d, uint16_t* h_out, int64_t ld_ho, uint32_t cols,
-                                                        uint32_t units_per_row, double eps, bool vec,
-                                                        double* inv_rms) {
+// inv_rms[row] = 1 / sqrt(sum(h'^2) / cols + eps) in float64 (the sum runs in
+// a fixed order: per-thread units in order, then a fixed butterfly and wave
+// order, so it is deterministic), then max |y| over y = bf16(h' * inv_rms),
+// formed exactly as NormSrc forms it (each thread reads back only the units
+// it wrote itself).  partial[b] = the workgroup's max, as bf16 magnitude
+// bits: the quantization pass folds these maxima, so every normalized value
+// is evaluated twice in all, not once per workgroup.
+__global__ __launch_bounds__(256) void norm_rows_kernel(const uint16_t* h, int64_t ld_h, const uint16_t* d,
+                                                        int64_t ld_d, uint16_t* h_out, int64_t ld_ho, uint32_t rows,
+                                                        uint32_t cols, uint32_t units_per_row, double eps, bool vec,
+                                                        double* inv_rms, uint32_t* partial) {
   __shared__ double wsum[4];
-  const uint32_t r = blockIdx.x;
-  const uint16_t* hrow = h + (int64_t)r * ld_h;
-  const uint16_t* drow = d ? d + (int64_t)r * ld_d : nullptr;
-  uint16_t* orow = d ? h_out + (int64_t)r * ld_ho : nullptr;
-  double acc = 0.0;
-  for (uint32_t u = threadIdx.x; u < units_per_row; u += blockDim.x) {
-    const uint32_t c0 = u * 8;
-    v4i hv = load8_bf16(hrow, c0, cols, vec);
-    if (drow != nullptr) {
-      const v4i dv = load8_bf16(drow, c0, cols, vec);
-      float f[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) f[i] = bf16_at(hv, i) + bf16_at(dv, i);
-      hv = pack8_bf16(f);
-      store8_bf16(orow, c0, cols, vec, hv);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const double x = bf16_at(hv, i);
-      acc = __builtin_fma(x, x, acc);
-    }
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  __shared__ uint32_t red[16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) wsum[wave] = acc;
-  __syncthreads();
-  if (threadIdx.x == 0) {
+  uint32_t m = 0;
+  for (uint32_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const uint16_t* hrow = h + (int64_t)r * ld_h;
+    const uint16_t* drow = d ? d + (int64_t)r * ld_d : nullptr;
+    uint16_t* orow = d ? h_out + (int64_t)r * ld_ho : nullptr;
+    double acc = 0.0;
+    for (uint32_t u = threadIdx.x; u < units_per_row; u += blockDim.x) {
+      const uint32_t c0 = u * 8;
+      v4i hv = load8_bf16(hrow, c0, cols, vec);
+      if (drow != nullptr) {
+        const v4i dv = load8_bf16(drow, c0, cols, vec);
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = bf16_at(hv, i) + bf16_at(dv, i);
+        hv = pack8_bf16(f);
+        store8_bf16(orow, c0, cols, vec, hv);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const double x = bf16_at(hv, i);
+        acc = __builtin_fma(x, x, acc);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (lane == 0) wsum[wave] = acc;
+    __syncthreads();
     double t = 0.0;
     for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += wsum[w];
-    inv_rms[r] = 1.0 / sqrt(t / (double)cols + eps);
+    const double g = 1.0 / sqrt(t / (double)cols + eps);
+    if (threadIdx.x == 0) inv_rms[r] = g;
+    const uint16_t* srow = d ? orow : hrow;
+    for (uint32_t u = threadIdx.x; u < units_per_row; u += blockDim.x) {
+      const v4i hv = load8_bf16(srow, u * 8, cols, vec);
+      double f[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[i] = (double)bf16_at(hv, i) * g;
+      m = max(m, absmax_bits8(pack8_bf16_f64(f)));
+    }
+    __syncthreads();  // wsum is rewritten for the next row
   }
+  m = block_max_u32(m, red);
+  if (threadIdx.x == 0) partial[blockIdx.x] = m;
 }
 
 __global__ void write_scale_kernel(float* scale_out, float v) { *scale_out = v; }
@@ -408,11 +433,11 @@ hipError_t launch_dynamic(const QuantArgs& a, const Src& src, bool small_ok, flo
     return hipGetLastError();
   }
   uint32_t* partial = static_cast<uint32_t*>(workspace);
-  const uint32_t grid = grid_for_units(a.total_units, 256 * kUnroll, kPartialBlocks);
+  const uint32_t grid = grid_for_units(a.total_units, 256 * Src::kUnitsPerThread, kPartialBlocks);
   absmax_partial_kernel<Src><<<grid, 256, 0, stream>>>(a, src, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const uint32_t grid2 = grid_for_units(a.total_units, 256 * kUnroll, 8192);
+  const uint32_t grid2 = grid_for_units(a.total_units, 256 * Src::kUnitsPerThread, 8192);
   quant_from_partial_kernel<F, Src><<<grid2, 256, 0, stream>>>(a, src, partial, grid, scale_out);
   return hipGetLastError();
 }
@@ -445,17 +470,23 @@ hipError_t launch_add_rmsnorm_quant(const uint16_t* h, int64_t ld_h, const uint1
     write_scale_kernel<<<1, 1, 0, stream>>>(scale_out, 1.0f);
     return hipGetLastError();
   }
+  uint32_t* partial = static_cast<uint32_t*>(workspace);
   double* inv_rms = reinterpret_cast<double*>(static_cast<uint8_t*>(workspace) + quant_workspace_bytes());
   const bool vec = rows16(h, ld_h) && (delta == nullptr || (rows16(delta, ld_delta) && rows16(h_out, ld_h_out)));
   const QuantArgs a = make_args(rows, cols, q, ld_q);
-  row_stats_kernel<<<(uint32_t)rows, 256, 0, stream>>>(h, ld_h, delta, ld_delta, h_out, ld_h_out, (uint32_t)cols,
-                                                        a.units_per_row, (double)eps, vec, inv_rms);
+  // launch 1: residual add, inv_rms and per-workgroup maxima of |y|
+  const uint32_t groups = (uint32_t)min(rows, (int64_t)kPartialBlocks);
+  norm_rows_kernel<<<groups, 256, 0, stream>>>(h, ld_h, delta, ld_delta, h_out, ld_h_out, (uint32_t)rows,
+                                               (uint32_t)cols, a.units_per_row, (double)eps, vec, inv_rms, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // launch 2: fold the maxima into the scale, quantize (y evaluated again)
   const uint16_t* hs = delta ? h_out : h;
   const int64_t ld_hs = delta ? ld_h_out : ld_h;
   const NormSrc src{hs, ld_hs, inv_rms, y_out, ld_y, rows16(hs, ld_hs), y_out != nullptr && rows16(y_out, ld_y)};
-  return launch_dynamic<kE4M3>(a, src, true, scale_out, workspace, stream);
+  const uint32_t grid2 = grid_for_units(a.total_units, 256 * NormSrc::kUnitsPerThread, 8192);
+  quant_from_partial_kernel<kE4M3, NormSrc><<<grid2, 256, 0, stream>>>(a, src, partial, groups, scale_out);
+  return hipGetLastError();
 }
 
 hipError_t launch_silu_mul_quant(const uint16_t* gu, int64_t ld_gu, int64_t rows, int64_t cols, uint16_t* y_out,
