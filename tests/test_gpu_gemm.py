@@ -55,6 +55,16 @@ def test_skinny_per_channel_llama_shapes(m, k, n):
     _run_and_check(d, True)
 
 
+@pytest.mark.parametrize("m,k,n", [(7, 8192, 1030), (3, 8208, 257), (16, 16384, 100)])
+def test_skinny_long_k_interleaved(m, k, n):
+    """K >= 8192 with weights under 32 MiB: K steps interleaved across the
+    waves, plain loads; ragged N and M, and a K whose last step is partial
+    (8208 = 32 steps of 256 + 16)."""
+    say("skinny long K", m, k, n)
+    d = _prepare(6, m, k, n, per_channel=True, outliers=True, rowmul=True, with_bias=(m == 3))
+    _run_and_check(d, True)
+
+
 @pytest.mark.parametrize("m,k,n", [(1, 1, 1), (2, 7, 3), (16, 100, 17), (9, 272, 33), (16, 16, 16), (4, 4099, 40)])
 def test_skinny_tiny_and_ragged_k(m, k, n):
     say("skinny ragged", m, k, n)

@@ -32,6 +32,8 @@ def _check_quant(y_ref_bits, q, s):
     (16, 4096, 4096, True),      # decode, one-launch quantization
     (16, 4096, 4096, False),
     (300, 4096, 4096, True),     # two-launch quantization
+    (2500, 512, 520, True),      # more rows than row groups: 2 or 3 rows per workgroup
+    (2500, 512, 512, False),
     (5, 1003, 1011, True),       # ragged row ends, odd pitch
     (1, 14336, 14336, True),
 ])
