@@ -1,4 +1,5 @@
-// Skinny-M scaled FP8 GEMM for decode (M <= 16), gfx950.
+// Skinny-M scaled FP8 GEMM for decode (M <= 64, 16 rows of M per workgroup),
+// gfx950.
 //
 // "[WIP] FP8 support" (text-generation-inference PR 1484), review discussion:
 // decode runs at fewer than 16 rows, wants a dedicated GEMV-like kernel, and
@@ -26,16 +27,17 @@
 // use the same lane/element -> k assignment, so products pair matching k
 // whatever order the hardware sums in.
 //
-// The waves of a workgroup split K into contiguous ranges of 256-byte steps,
-// keep two steps of loads in flight, and are summed through LDS in a fixed
-// order, so results do not depend on timing.  The rescale
+// The waves of a workgroup split K into 256-byte steps (contiguous ranges,
+// or every fourth step for long K), run a rolling pipeline with the next
+// step's loads in flight while they work on the current one, and are summed
+// through LDS in a fixed order, so results do not depend on timing.  The rescale
 // epilogue out = acc * (s_a * s_w[n]) + bias[n] -> bf16 is applied in the
 // store ("[Kernel] Implement fallback for FP8 channelwise using
 // torch._scaled_mm", description: the channelwise rescale follows the
 // per-tensor GEMM; fused here instead of a separate pass).
 //
-// Larger M runs the same kernels over a grid of 16-row blocks of M; that is
-// the fallback for layouts the matrix-core GEMM does not take.  Layouts that
+// M up to 64 runs the same kernels over a grid of 16-row blocks of M, and so
+// does any M for layouts the matrix-core GEMM does not take.  Layouts that
 // are not 16-byte aligned (or K % 16 != 0) use a byte-granular variant that
 // loads each lane's 32 bytes directly in the matrix-core layout.
 

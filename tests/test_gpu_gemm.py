@@ -39,7 +39,7 @@ def _run_and_check(d, per_channel, rows=None, accum="fp32"):
                              bias_bits=d["bias_bits"], accum=accum), out
 
 
-# ------------------------------------------------------------- skinny (M <= 16)
+# ------------------------------------------------------------- skinny (M <= 64)
 @pytest.mark.parametrize("m", [1, 3, 7, 13, 16])
 @pytest.mark.parametrize("k,n", [(4096, 4100), (4096, 1030), (4096, 4096)])
 def test_skinny_per_tensor_unaligned(m, k, n):
