@@ -73,8 +73,12 @@ def test_skinny_tiny_and_ragged_k(m, k, n):
 
 
 # -------------------------------------------------- mid M (skinny over M blocks)
-@pytest.mark.parametrize("m,k,n", [(17, 4096, 1030), (33, 512, 4100), (64, 1024, 300)])
+@pytest.mark.parametrize("m,k,n", [(17, 4096, 1030), (33, 512, 4100), (64, 1024, 300),
+                                   (40, 14336, 2401), (20, 4096, 8200)])
 def test_mid_m(m, k, n):
+    """16 < M <= 64 on the skinny kernel; the last two shapes have at least
+    32 MiB of weights (non-temporal loads), with interleaved and with
+    contiguous K steps, a ragged N and a partial last block of M."""
     say("mid m", m, k, n)
     d = _prepare(4, m, k, n, per_channel=False, with_bias=True)
     _run_and_check(d, False)
