@@ -66,6 +66,8 @@ def test_add_rmsnorm_quant(rows, cols, pitch, with_delta):
     (16, 14336, 2 * 14336),      # decode gate_up output
     (64, 14336, 2 * 14336),
     (3, 1001, 2 * 1001 + 5),     # ragged, odd pitch (unaligned up half)
+    (300, 14336, 2 * 14336),     # >= 4 Mi elements: the float32 path with its float64 fallback
+    (4100, 1030, 2 * 1030 + 3),  # the same, unaligned
 ])
 def test_silu_mul_quant(rows, cols, pitch):
     say("silu_mul_quant", rows, cols, pitch)
