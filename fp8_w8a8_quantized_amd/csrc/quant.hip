@@ -168,16 +168,16 @@ struct NormSrc {
 
 // bf16(g / (1 + exp(-g)) * u) as evaluated in float64 and rounded once,
 // computed in float32 where that provably gives the same bf16.  The float32
-// value (expf, add, divide, multiply: within 5 float32 ulps of the exact
-// one for g > -80, where every intermediate is a normal number) rounds to
-// the same bf16 as the exact value unless it lies within 5 ulps of a bf16
-// rounding midpoint, i.e. unless its low 16 bits are within 5 of 0x8000;
-// there (with a margin of 32), for g <= -80 (expf nears overflow), and for
-// results below 2^-100 the float64 expression decides.  That is about 0.1%
-// of the values.
+// value (expf within 1 ulp, the add, v_rcp_f32 within 1 ulp, two multiplies:
+// within 8 float32 ulps of the exact one for g > -80, where every
+// intermediate is a normal number) rounds to the same bf16 as the exact
+// value unless it lies within 8 ulps of a bf16 rounding midpoint, i.e.
+// unless its low 16 bits are within 8 of 0x8000; there (with a margin of
+// 32), for g <= -80 (expf nears overflow), and for results below 2^-100 the
+// float64 expression decides.  That is about 0.1% of the values.
 constexpr uint32_t kSiluMargin = 32;
 __device__ __forceinline__ uint32_t silu_mul_bf16(float g, float u) {
-  const float y = g / (1.0f + expf(-g)) * u;
+  const float y = g * __builtin_amdgcn_rcpf(1.0f + expf(-g)) * u;
   const uint32_t low = __float_as_uint(y) & 0xffffu;
   const bool near_mid = low - (0x8000u - kSiluMargin) <= 2 * kSiluMargin;
   const bool tiny = fabsf(y) < 0x1p-100f && g != 0.0f && u != 0.0f;
@@ -191,7 +191,7 @@ __device__ __forceinline__ uint32_t silu_mul_bf16(float g, float u) {
 // Gated activation, gate half first: y = bf16(silu(g) * u) with
 // silu(g) = g / (1 + exp(-g)), the float64 value rounded once to bf16.
 // FAST: through silu_mul_bf16 (same bits).  Measured at a prefill size
-// (16384 x 14336) the quantization takes 708 us with it and 968 us without;
+// (16384 x 14336) the quantization takes 627 us with it and 968 us without;
 // at a decode size (16 x 14336), where the float64 branches of a few lanes
 // hold up whole waves, 8.6 us with it and 7.8 us without.
 template <bool FAST>
