@@ -207,7 +207,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
   };
 
   const int KT = (g.K + BK - 1) / BK;
-  // L2 prefetch of step s of tile t, PF_DIST steps ahead of the step it
+  // L2 prefetch of step s of tile t, kPrefetchDist steps ahead of the step it
   // feeds.  The 32 workgroups an XCD runs at once hold 8 tile-rows x 4
   // tile-columns (see tile_at), so they share 8 A panels (4 tiles each) and
   // 4 W panels (8 tiles each): this one touches rows 64 (tn % 4) .. + 63 of
