@@ -96,6 +96,20 @@ def test_mfma_gemm(m, k, n, pc, accum):
 
 
 @pytest.mark.parametrize("accum", ["fp32", "fp8"])
+@pytest.mark.parametrize("k,n", [(128, 4104), (256, 4101), (400, 4104)])
+def test_mfma_gemm_several_tiles_per_workgroup_short_k(k, n, accum):
+    """17 x 17 tiles (more than one per workgroup on a 256-CU part) with one,
+    two and four (ragged) k steps per tile, vector and scalar output stores:
+    the wait counts at tile changes (stores still in flight, the fp8 mode's
+    prefetch loads) and the next tile's first step loaded during the last."""
+    m = 4352
+    say("mfma several tiles", m, k, n, accum)
+    d = _prepare(5, m, k, n, per_channel=True, rowmul=True, with_bias=True)
+    rows = np.r_[0:m:7, m - 9:m]
+    _run_and_check(d, True, rows=rows, accum=accum)
+
+
+@pytest.mark.parametrize("accum", ["fp32", "fp8"])
 def test_mfma_gemm_k_not_multiple_of_128(accum):
     d = _prepare(3, 320, 4096 + 48, 512, per_channel=True, rowmul=True)
     _run_and_check(d, True, accum=accum)
