@@ -153,6 +153,27 @@ def test_unaligned_layout_falls_back_correctly():
     assert np.all(ob[:, :3] == -7.0) and np.all(ob[:, n + 3:] == -7.0)
 
 
+@pytest.mark.parametrize("accum", ["fp32", "fp8"])
+def test_mfma_padded_pitches_and_output_view(accum):
+    """Matrix-core path with row pitches larger than K and N (16-byte
+    multiples), a k tail, several tiles, and an output sub-view whose guard
+    columns must stay untouched."""
+    m, k, n = 600, 1040, 520
+    x = synth.activations(9, m, k, outliers=True); w = synth.weights(9, n, k, row_multipliers=True)
+    b = synth.bias(9, n)
+    a_q, s_a = fp8.quant_dynamic(dev_bf16(x), q=torch.empty((m, 1072), dtype=torch.uint8, device="cuda")[:, :k])
+    w_q, s_w = fp8.quant_dynamic_per_row(dev_bf16(w), q=torch.empty((n, 1056), dtype=torch.uint8, device="cuda")[:, :k])
+    outbuf = torch.full((m, 536 + 16), -7.0, dtype=torch.bfloat16, device="cuda")
+    out = fp8.scaled_mm(a_q, w_q, s_a, s_w, True, dev_bf16(b), out=outbuf[:, 8:8 + n], accum=accum)
+    torch.cuda.synchronize()
+    aq, sa = oracle.quant_dynamic(x); wq, sw = oracle.quant_weight(w, True)
+    assert np.array_equal(host_u8(a_q), aq) and np.array_equal(host_u8(w_q), wq)
+    ref = oracle.scaled_mm(aq, wq, sa, sw, True, b)
+    assert_gemm_close(host_bf16_bits(out), ref, aq, sa, wq, sw, True, bias_bits=b, accum=accum)
+    ob = outbuf.float().cpu().numpy()
+    assert np.all(ob[:, :8] == -7.0) and np.all(ob[:, 8 + n:] == -7.0)
+
+
 # -------------------------------------------------------------- invariants
 @pytest.mark.parametrize("m,n", [(16, 4096), (512, 1024)])
 def test_per_channel_equal_scales_bit_exact_with_per_tensor(m, n):
