@@ -55,6 +55,16 @@ def test_skinny_per_channel_llama_shapes(m, k, n):
     _run_and_check(d, True)
 
 
+@pytest.mark.parametrize("m,k,n,pc", [(16, 4096, 16400, True), (3, 2048, 16392, False), (13, 1024, 16400, True),
+                                      (16, 4096, 28672, False)])
+def test_skinny_two_blocks_per_wave(m, k, n, pc):
+    """N >= 16384 with K < 8192: two 16-row weight blocks per wave, with a
+    last block partly or wholly past N, plain and non-temporal weight loads."""
+    say("skinny two blocks", m, k, n, pc)
+    d = _prepare(6, m, k, n, per_channel=pc, rowmul=pc, with_bias=pc)
+    _run_and_check(d, pc)
+
+
 @pytest.mark.parametrize("m,k,n", [(7, 8192, 1030), (3, 8208, 257), (16, 16384, 100)])
 def test_skinny_long_k_interleaved(m, k, n):
     """K >= 8192 with weights under 32 MiB: K steps interleaved across the
