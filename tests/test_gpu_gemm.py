@@ -57,10 +57,10 @@ def test_skinny_per_channel_llama_shapes(m, k, n):
 
 @pytest.mark.parametrize("m,k,n,pc", [(16, 4096, 16400, True), (3, 2048, 16392, False), (13, 1024, 16400, True),
                                       (16, 4096, 28672, False)])
-def test_skinny_two_blocks_per_wave(m, k, n, pc):
-    """N >= 16384 with K < 8192: two 16-row weight blocks per wave, with a
-    last block partly or wholly past N, plain and non-temporal weight loads."""
-    say("skinny two blocks", m, k, n, pc)
+def test_skinny_large_n_ragged(m, k, n, pc):
+    """N of 16384 and more with K below 8192: a last 16-row block partly past
+    N, plain and non-temporal weight loads, per-tensor and channelwise."""
+    say("skinny large n", m, k, n, pc)
     d = _prepare(6, m, k, n, per_channel=pc, rowmul=pc, with_bias=pc)
     _run_and_check(d, pc)
 
