@@ -235,8 +235,9 @@ def main():
                          "many MiB, so that profiler byte counters can be scaled against kernels of known traffic")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the layer would shard column-parallel over N; see the design notes).", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the layer would shard column-parallel over N, each GPU holding a slice of the weight rows "
+              "and their scales).", file=sys.stderr)
         sys.exit(2)
     if args.workload == "chain":
         return run_chain(args)

@@ -12,8 +12,8 @@ The method, from the pages:
     served by a per-tensor scaled GEMM followed by a rescale of each output
     column.
 
-Readings where the pages are silent (each is listed with its reason in the
-design notes): the dynamic scale is amax/448 rounded once to float32, with
+Readings where the pages are silent: the dynamic scale is amax/448 rounded
+once to float32 (448 being the largest finite e4m3fn value), with
 amax == 0 mapping to scale 1.0; values are divided (not multiplied by a
 reciprocal) in float32; the cast saturates and rounds to nearest even; the
 weight has nn.Linear layout [N, K] and output channel n is weight row n; an
