@@ -137,9 +137,15 @@ def cpu_baseline(m, lin_shapes, row_frac=8, budget_s=10.0):
             done_bytes += quant_bytes(m, k) + gemm_bytes(m, k, ns)
             done_flops += 2 * m * k * ns
         steps += 1
+    cpu = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
+    except OSError:
+        pass
     desc = (f"{steps} oracle steps over the 4 linears at M={m} with N/{row_frac} output channels each "
             f"({timed:.1f} s timed; weight quantization untimed; element-wise NumPy on 1 thread, "
-            f"fp64 BLAS matmul on {threads})")
+            f"fp64 BLAS matmul on {threads}; {cpu}, {os.cpu_count()} logical CPUs visible)")
     return done_bytes, done_flops, timed, threads, desc
 
 
