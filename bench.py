@@ -330,7 +330,7 @@ def main():
         value = step_bytes / (ms_per_step * 1e-3) / 1e9
         unit = "GB/s"
         achieved = per_launch_bytes / avg_launch_s / 1e9
-        kernel = "gemm_skinny_kernel<4, 2, {false|true}, {false|true}, 0, 0>"
+        kernel = "gemm_skinny_kernel<4, 2, {false|true}, {false|true}, 0, 0> + gemm_skinny2_kernel<4, 1, true, 0, 0>"
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(kernel),
                 "kernel": kernel, "avg_launch_us": round(avg_launch_s * 1e6, 2),
