@@ -30,6 +30,8 @@
 // aligned output rows; a row's ragged end and unaligned layouts use
 // element-wise loads and stores.
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -286,7 +288,12 @@ __device__ __forceinline__ void quant_range(const QuantArgs& a, const Src& src, 
 // whole tensor.
 constexpr int kSmallThreads = 512;
 constexpr int kSmallBatch = 16;
-template <int F, class Src>
+// BUF (plain bf16 source, 16-byte aligned rows, cols % 8 == 0, the tensor
+// under 2 GiB): the batch's offsets are computed first and its 16 loads go
+// out back to back as unconditional buffer loads (units past the end get an
+// out-of-range offset and read zeros), one wait for all of them.  With a
+// conditional load per unit the compiler waited for each in turn.
+template <int F, class Src, bool BUF>
 __global__ __launch_bounds__(kSmallThreads) void quant_dynamic_small_kernel(QuantArgs a, Src src, float* scale_out) {
   __shared__ uint32_t red[16];
   const uint32_t T = a.total_units;
@@ -295,14 +302,31 @@ __global__ __launch_bounds__(kSmallThreads) void quant_dynamic_small_kernel(Quan
   v4i keep = {0, 0, 0, 0};
   for (uint32_t j0 = 0; j0 < slots; j0 += kSmallBatch) {
     v4i v[kSmallBatch];
+    if constexpr (BUF) {
+      const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)src.x, (short)0, (int)(((int64_t)(a.rows - 1) * src.ld + a.cols) * 2), kRsrcWord3);
+      uint32_t off[kSmallBatch];
 #pragma unroll
-    for (int i = 0; i < kSmallBatch; ++i) {
-      const uint32_t u = threadIdx.x + (j0 + i) * kSmallThreads;
-      v[i] = v4i{0, 0, 0, 0};
-      if (u < T) {
+      for (int i = 0; i < kSmallBatch; ++i) {
+        const uint32_t u = threadIdx.x + (j0 + i) * kSmallThreads;
         uint32_t r, c0;
         unit_coords(a, u, r, c0);
-        v[i] = src.load(a, r, c0);
+        off[i] = u < T ? (uint32_t)((r * (uint32_t)src.ld + c0) * 2) : kOutOfRange;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < kSmallBatch; ++i)
+        v[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off[i], 0, 0));
+    } else {
+#pragma unroll
+      for (int i = 0; i < kSmallBatch; ++i) {
+        const uint32_t u = threadIdx.x + (j0 + i) * kSmallThreads;
+        v[i] = v4i{0, 0, 0, 0};
+        if (u < T) {
+          uint32_t r, c0;
+          unit_coords(a, u, r, c0);
+          v[i] = src.load(a, r, c0);
+        }
       }
     }
 #pragma unroll
@@ -466,7 +490,13 @@ hipError_t launch_dynamic(const QuantArgs& a, const Src& src, bool small_ok, flo
   if (small_ok && a.total_units <= kSmallUnits) {
     // one workgroup per 512-unit slot: at most kSmallUnits / 512 = 32
     const uint32_t grid = (a.total_units + kSmallThreads - 1) / kSmallThreads;
-    quant_dynamic_small_kernel<F, Src><<<grid, kSmallThreads, 0, stream>>>(a, src, scale_out);
+    if constexpr (std::is_same<Src, PlainSrc>::value) {
+      if (src.vec && a.cols % 8 == 0 && (int64_t)a.rows * src.ld * 2 < (int64_t(1) << 31)) {
+        quant_dynamic_small_kernel<F, Src, true><<<grid, kSmallThreads, 0, stream>>>(a, src, scale_out);
+        return hipGetLastError();
+      }
+    }
+    quant_dynamic_small_kernel<F, Src, false><<<grid, kSmallThreads, 0, stream>>>(a, src, scale_out);
     return hipGetLastError();
   }
   uint32_t* partial = static_cast<uint32_t*>(workspace);
