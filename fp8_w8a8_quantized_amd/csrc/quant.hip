@@ -232,20 +232,46 @@ struct SiluMulSrc {
 };
 
 // max |x| bits over units u0, u0 + stride, ... < u1, UNROLL loads in flight
-template <class Src, int UNROLL = kUnroll>
+// N units u, u + stride, ... of a plain bf16 source with aligned rows and
+// cols % 8 == 0: offsets first, then N unconditional buffer loads back to
+// back (units at or past u1 get an out-of-range offset and read zeros).
+template <int N>
+__device__ __forceinline__ void load_units_buf(const QuantArgs& a, const PlainSrc& src, uint32_t u, uint32_t u1,
+                                               uint32_t stride, v4i (&v)[N], uint32_t (&r)[N], uint32_t (&c0)[N]) {
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)src.x, (short)0, (int)(((int64_t)(a.rows - 1) * src.ld + a.cols) * 2), kRsrcWord3);
+  uint32_t off[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const uint32_t uu = u + i * stride;
+    unit_coords(a, uu, r[i], c0[i]);
+    off[i] = uu < u1 ? (uint32_t)((r[i] * (uint32_t)src.ld + c0[i]) * 2) : kOutOfRange;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    v[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off[i], 0, 0));
+}
+
+template <class Src, bool BUF = false, int UNROLL = kUnroll>
 __device__ __forceinline__ uint32_t absmax_range(const QuantArgs& a, const Src& src, uint32_t u0, uint32_t u1,
                                                  uint32_t stride) {
   uint32_t m = 0;
   for (uint32_t u = u0; u < u1; u += stride * UNROLL) {
     v4i v[UNROLL];
+    if constexpr (BUF) {
+      uint32_t r[UNROLL], c0[UNROLL];
+      load_units_buf<UNROLL>(a, src, u, u1, stride, v, r, c0);
+    } else {
 #pragma unroll
-    for (int i = 0; i < UNROLL; ++i) {
-      const uint32_t uu = u + i * stride;
-      v[i] = v4i{0, 0, 0, 0};
-      if (uu < u1) {
-        uint32_t r, c0;
-        unit_coords(a, uu, r, c0);
-        v[i] = src.load(a, r, c0);
+      for (int i = 0; i < UNROLL; ++i) {
+        const uint32_t uu = u + i * stride;
+        v[i] = v4i{0, 0, 0, 0};
+        if (uu < u1) {
+          uint32_t r, c0;
+          unit_coords(a, uu, r, c0);
+          v[i] = src.load(a, r, c0);
+        }
       }
     }
 #pragma unroll
@@ -254,19 +280,23 @@ __device__ __forceinline__ uint32_t absmax_range(const QuantArgs& a, const Src& 
   return m;
 }
 
-template <int F, class Src>
+template <int F, class Src, bool BUF = false>
 __device__ __forceinline__ void quant_range(const QuantArgs& a, const Src& src, uint32_t u0, uint32_t u1,
                                             uint32_t stride, float s) {
   for (uint32_t u = u0; u < u1; u += stride * kUnroll) {
     v4i v[kUnroll];
     uint32_t r[kUnroll], c0[kUnroll];
+    if constexpr (BUF) {
+      load_units_buf<kUnroll>(a, src, u, u1, stride, v, r, c0);
+    } else {
 #pragma unroll
-    for (int i = 0; i < kUnroll; ++i) {
-      const uint32_t uu = u + i * stride;
-      r[i] = 0; c0[i] = 0; v[i] = v4i{0, 0, 0, 0};
-      if (uu < u1) {
-        unit_coords(a, uu, r[i], c0[i]);
-        v[i] = src.load(a, r[i], c0[i]);
+      for (int i = 0; i < kUnroll; ++i) {
+        const uint32_t uu = u + i * stride;
+        r[i] = 0; c0[i] = 0; v[i] = v4i{0, 0, 0, 0};
+        if (uu < u1) {
+          unit_coords(a, uu, r[i], c0[i]);
+          v[i] = src.load(a, r[i], c0[i]);
+        }
       }
     }
 #pragma unroll
@@ -348,16 +378,17 @@ __global__ __launch_bounds__(kSmallThreads) void quant_dynamic_small_kernel(Quan
 }
 
 // Launch 1 of 2: per-block maxima of |x| (as bf16 magnitude bits).
-template <class Src>
+template <class Src, bool BUF = false>
 __global__ __launch_bounds__(256) void absmax_partial_kernel(QuantArgs a, Src src, uint32_t* partial) {
   __shared__ uint32_t red[16];
-  uint32_t m = absmax_range(a, src, blockIdx.x * blockDim.x + threadIdx.x, a.total_units, gridDim.x * blockDim.x);
+  uint32_t m = absmax_range<Src, BUF>(a, src, blockIdx.x * blockDim.x + threadIdx.x, a.total_units,
+                                      gridDim.x * blockDim.x);
   m = block_max_u32(m, red);
   if (threadIdx.x == 0) partial[blockIdx.x] = m;
 }
 
 // Launch 2 of 2: fold the maxima, derive the scale, quantize.
-template <int F, class Src>
+template <int F, class Src, bool BUF = false>
 __global__ __launch_bounds__(256) void quant_from_partial_kernel(QuantArgs a, Src src, const uint32_t* partial,
                                                                   uint32_t nparts, float* scale_out) {
   __shared__ uint32_t red[16];
@@ -366,7 +397,7 @@ __global__ __launch_bounds__(256) void quant_from_partial_kernel(QuantArgs a, Sr
   m = block_max_u32(m, red);
   const float s = scale_from_amax<F>(bf16_to_f32(m));
   if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
-  quant_range<F>(a, src, blockIdx.x * blockDim.x + threadIdx.x, a.total_units, gridDim.x * blockDim.x, s);
+  quant_range<F, Src, BUF>(a, src, blockIdx.x * blockDim.x + threadIdx.x, a.total_units, gridDim.x * blockDim.x, s);
 }
 
 template <int F>
@@ -501,10 +532,19 @@ hipError_t launch_dynamic(const QuantArgs& a, const Src& src, bool small_ok, flo
   }
   uint32_t* partial = static_cast<uint32_t*>(workspace);
   const uint32_t grid = grid_for_units(a.total_units, 256 * Src::kUnitsPerThread, kPartialBlocks);
+  const uint32_t grid2 = grid_for_units(a.total_units, 256 * Src::kUnitsPerThread, 8192);
+  if constexpr (std::is_same<Src, PlainSrc>::value) {
+    if (src.vec && a.cols % 8 == 0 && (int64_t)a.rows * src.ld * 2 < (int64_t(1) << 31)) {
+      absmax_partial_kernel<Src, true><<<grid, 256, 0, stream>>>(a, src, partial);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      quant_from_partial_kernel<F, Src, true><<<grid2, 256, 0, stream>>>(a, src, partial, grid, scale_out);
+      return hipGetLastError();
+    }
+  }
   absmax_partial_kernel<Src><<<grid, 256, 0, stream>>>(a, src, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const uint32_t grid2 = grid_for_units(a.total_units, 256 * Src::kUnitsPerThread, 8192);
   quant_from_partial_kernel<F, Src><<<grid2, 256, 0, stream>>>(a, src, partial, grid, scale_out);
   return hipGetLastError();
 }
