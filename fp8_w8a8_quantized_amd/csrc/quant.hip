@@ -313,7 +313,8 @@ __device__ __forceinline__ void quant_range(const QuantArgs& a, const Src& src, 
 // slot it will quantize -- units blockIdx.x * 512 + threadIdx.x -- so the
 // codes need no second read.  The grid has one workgroup per slot (at most
 // 32); workgroup 0 writes the scale.  (Measured on the 16 x 4096 decode
-// input: 5.2 us per launch, against 5.4 us with 1024 threads x 8 loads.)
+// input: 4.3 us per launch with the buffer-load batches below, 5.1 us with
+// a conditional load per unit, 5.4 us with 1024 threads x 8 loads.)
 // Only for cheap sources: every workgroup evaluates the source over the
 // whole tensor.
 constexpr int kSmallThreads = 512;
