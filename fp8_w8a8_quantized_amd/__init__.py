@@ -41,6 +41,9 @@ SIGNATURES = {
     "fp8_add_rmsnorm_quant_dynamic": (_I, [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, ctypes.c_float,
                                            _P, _I64, _P, _I64, _P, _P, _P]),
     "fp8_silu_mul_quant_dynamic": (_I, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _P, _P]),
+    "fp8_linear_workspace_bytes": (ctypes.c_size_t, []),
+    "fp8_linear_dynamic": (_I, [_P, _I64, _P, _I64, _P, _I, _I, _P, _P, _I64, _P, _P, _I64, _I64, _I64, _I64,
+                                _P, _P]),
 }
 
 _lib = None
@@ -167,8 +170,51 @@ def scaled_mm(a_q, w_q, s_a, s_w, per_channel, bias=None, out=None, accum="fp32"
     return out
 
 
+def linear_workspace_bytes():
+    return int(lib().fp8_linear_workspace_bytes())
+
+
+def new_linear_workspace(device=None):
+    """Scratch workspace of linear_dynamic (no initialization needed)."""
+    return torch.empty(linear_workspace_bytes(), dtype=torch.uint8, device=device or "cuda")
+
+
+def linear_dynamic(x, w_q, s_w, per_channel, bias=None, workspace=None, a_q=None, s_a=None, out=None,
+                   accum="fp32"):
+    """The whole e4m3 W8A8 linear in one library call: dynamic per-tensor
+    quantization of bf16 x [M, K] (codes a_q, scale s_a), then the scaled
+    GEMM against w_q [N, K].
+
+    Returns (out [M, N] bf16, a_q [M, K] uint8, s_a [1] float32).
+    """
+    _mat(x, "x", torch.bfloat16)
+    _mat(w_q, "w_q", torch.uint8)
+    M, K = x.shape
+    N, K2 = w_q.shape
+    if K != K2:
+        raise ValueError(f"K mismatch: x has {K}, w_q has {K2}")
+    dev = x.device
+    a_q = torch.empty((M, K), dtype=torch.uint8, device=dev) if a_q is None else a_q
+    s_a = torch.empty(1, dtype=torch.float32, device=dev) if s_a is None else s_a
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if out is None else out
+    workspace = new_linear_workspace(dev) if workspace is None else workspace
+    mode = FP8_SCALE_PER_CHANNEL if per_channel else FP8_SCALE_PER_TENSOR
+    _check(lib().fp8_linear_dynamic(_ptr(x), x.stride(0), _ptr(w_q), w_q.stride(0), _ptr(s_w), mode, ACCUM[accum],
+                                    _ptr(bias), _ptr(a_q), a_q.stride(0), _ptr(s_a), _ptr(out), out.stride(0),
+                                    M, N, K, _ptr(workspace), _stream()),
+           "fp8_linear_dynamic")
+    return out, a_q, s_a
+
+
 def linear(x, w_q, s_w, per_channel, bias=None, workspace=None, accum="fp32", fmt_a="e4m3", fmt_w="e4m3"):
-    """The W8A8 linear: dynamic activation quantization then scaled GEMM."""
+    """The W8A8 linear: dynamic activation quantization then scaled GEMM.
+
+    e4m3 codes on both sides go through linear_dynamic (one library call);
+    other formats make the two calls.  workspace: a new_workspace() (or a
+    new_linear_workspace(), the same size).
+    """
+    if fmt_a == "e4m3" and fmt_w == "e4m3":
+        return linear_dynamic(x, w_q, s_w, per_channel, bias, workspace=workspace, accum=accum)[0]
     a_q, s_a = quant_dynamic(x, workspace=workspace, fmt=fmt_a)
     return scaled_mm(a_q, w_q, s_a, s_w, per_channel, bias, accum=accum, fmt_a=fmt_a, fmt_w=fmt_w)
 

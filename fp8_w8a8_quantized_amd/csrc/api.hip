@@ -199,6 +199,38 @@ fp8_status fp8_scaled_mm_fmt(const uint8_t* a_q, int64_t lda, fp8_format fmt_a, 
   return FP8_OK;
 }
 
+size_t fp8_linear_workspace_bytes(void) { return fp8w8a8::quant_workspace_bytes(); }
+
+fp8_status fp8_linear_dynamic(const uint16_t* x_bf16, int64_t ld_x, const uint8_t* w_q, int64_t ldw,
+                              const float* s_w, fp8_scale_mode mode, fp8_accum_mode accum,
+                              const uint16_t* bias_bf16, uint8_t* a_q, int64_t ld_aq, float* s_a_out,
+                              uint16_t* out_bf16, int64_t ldo, int64_t M, int64_t N, int64_t K, void* workspace,
+                              void* stream) {
+  const char* fn = "fp8_linear_dynamic";
+  if (M < 0 || N < 0) return fail(FP8_ERR_INVALID_ARG, "%s: negative M or N (M=%lld, N=%lld)", fn,
+                                  (long long)M, (long long)N);
+  if (K < 1) return fail(FP8_ERR_INVALID_ARG, "%s: K must be >= 1 (K=%lld)", fn, (long long)K);
+  if (ld_x < K || ld_aq < K || ldw < K) return fail(FP8_ERR_INVALID_ARG, "%s: ld_x/ld_aq/ldw smaller than K", fn);
+  if (ldo < N) return fail(FP8_ERR_INVALID_ARG, "%s: ldo smaller than N", fn);
+  if (mode != FP8_SCALE_PER_TENSOR && mode != FP8_SCALE_PER_CHANNEL)
+    return fail(FP8_ERR_INVALID_ARG, "%s: unknown scale mode %d", fn, (int)mode);
+  if (accum != FP8_ACCUM_FP32 && accum != FP8_ACCUM_FP8_MFMA)
+    return fail(FP8_ERR_INVALID_ARG, "%s: unknown accumulation mode %d", fn, (int)accum);
+  // pointers the problem touches: x and a_q when M > 0, the GEMM's when M and N are
+  if (s_a_out == nullptr || (M > 0 && (x_bf16 == nullptr || a_q == nullptr || workspace == nullptr)) ||
+      (M > 0 && N > 0 && (w_q == nullptr || s_w == nullptr || out_bf16 == nullptr)))
+    return fail(FP8_ERR_INVALID_ARG, "%s: null required pointer", fn);
+  if (M >= (1ll << 31) || N >= (1ll << 31) || K >= (1ll << 30) || ldw >= (1ll << 40) || ld_aq >= (1ll << 40) ||
+      M * ((K + 7) / 8) >= (1ll << 31))
+    return fail(FP8_ERR_UNSUPPORTED, "%s: problem too large", fn);
+  // the quantization, then the GEMM on its codes (nothing to multiply for M == 0 or N == 0)
+  fp8_status st = hip_status(fp8w8a8::launch_quant_dynamic(x_bf16, M, K, ld_x, FP8_FORMAT_E4M3, a_q, ld_aq,
+                                                           s_a_out, workspace, static_cast<hipStream_t>(stream)),
+                             fn);
+  if (st != FP8_OK || M == 0 || N == 0) return st;
+  return fp8_scaled_mm(a_q, ld_aq, w_q, ldw, s_a_out, s_w, mode, accum, bias_bf16, out_bf16, ldo, M, N, K, stream);
+}
+
 fp8_status fp8_scaled_mm(const uint8_t* a_q, int64_t lda, const uint8_t* w_q, int64_t ldw, const float* s_a,
                          const float* s_w, fp8_scale_mode mode, fp8_accum_mode accum, const uint16_t* bias_bf16,
                          uint16_t* out_bf16, int64_t ldo, int64_t M, int64_t N, int64_t K, void* stream) {

@@ -173,6 +173,33 @@ fp8_status fp8_scaled_mm(const uint8_t* a_q, int64_t lda, const uint8_t* w_q, in
                          int64_t ldo, int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
+ * The whole W8A8 linear in one call: dynamic per-tensor quantization of the
+ * bf16 activations (exactly fp8_quant_dynamic: s_a = amax / 448, codes into
+ * a_q) followed by fp8_scaled_mm on those codes with that scale ("Prototype
+ * FP8Linear W8A8 runtime quantization", opening post: both steps run at
+ * every call).  Outputs are bit-identical to making the two calls.
+ *
+ *   x      [M, K] bf16, row pitch ld_x >= K           (activations, input)
+ *   w_q, ldw, s_w, mode, accum, bias, out, ldo        as in fp8_scaled_mm
+ *   a_q    [M, K] e4m3fn, row pitch ld_aq >= K        (codes, output)
+ *   s_a_out 1 float                                    (scale, output)
+ *   workspace  fp8_linear_workspace_bytes() of device memory, no
+ *          initialization needed (scratch of the quantization, as for
+ *          fp8_quant_dynamic).
+ * Errors: INVALID_ARG for a null s_a_out, a null x, a_q or workspace with
+ * M > 0, a null w_q, s_w or out with M > 0 and N > 0 (bias may always be
+ * NULL), negative M or N, K < 1, a pitch below its minimum, or an unknown
+ * scale or accumulation mode; UNSUPPORTED for sizes past the limits of
+ * fp8_quant_dynamic and fp8_scaled_mm.
+ */
+size_t fp8_linear_workspace_bytes(void);
+fp8_status fp8_linear_dynamic(const uint16_t* x_bf16, int64_t ld_x, const uint8_t* w_q, int64_t ldw,
+                              const float* s_w, fp8_scale_mode mode, fp8_accum_mode accum,
+                              const uint16_t* bias_bf16, uint8_t* a_q, int64_t ld_aq, float* s_a_out,
+                              uint16_t* out_bf16, int64_t ldo, int64_t M, int64_t N, int64_t K,
+                              void* workspace, void* stream);
+
+/*
  * Producer-fused quantization: the step that feeds a linear, computed and
  * quantized in the same pass, so its bf16 result never travels through
  * memory.  The review of "[WIP] FP8 support" (text-generation-inference PR

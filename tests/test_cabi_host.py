@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
         "fp8_quant_workspace_bytes", "fp8_quant_dynamic", "fp8_quant_static",
         "fp8_quant_dynamic_per_row", "fp8_scaled_mm", "fp8_last_error",
         "fp8_norm_quant_workspace_bytes", "fp8_add_rmsnorm_quant_dynamic", "fp8_silu_mul_quant_dynamic",
-        "fp8_quant_dynamic_fmt", "fp8_quant_static_fmt", "fp8_quant_dynamic_per_row_fmt", "fp8_scaled_mm_fmt"])
+        "fp8_quant_dynamic_fmt", "fp8_quant_static_fmt", "fp8_quant_dynamic_per_row_fmt", "fp8_scaled_mm_fmt",
+        "fp8_linear_workspace_bytes", "fp8_linear_dynamic"])
 
 
 def test_library_exports_every_declared_function(lib):
@@ -133,3 +134,27 @@ def test_format_arguments_are_validated(lib):
     assert f(P, 64, 0, P, 64, 3, P, P, 0, 0, NULL, P, 32, 4, 32, 64, NULL) == INVALID
     assert f(P, 64, 5, P, 64, 1, P, P, 0, 0, NULL, P, 32, 4, 32, 64, NULL) == INVALID
     assert f(P, 63, 1, P, 64, 1, P, P, 0, 0, NULL, P, 32, 4, 32, 64, NULL) == INVALID   # lda < K
+
+
+def test_linear_dynamic_rejects_bad_arguments(lib):
+    f = lib.fp8_linear_dynamic
+    good = dict(x=P, ldx=64, w=P, ldw=64, sw=P, mode=1, accum=0, bias=NULL, aq=P, ldaq=64, sa=P, out=P, ldo=32,
+                M=4, N=32, K=64, ws=P)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return f(a["x"], a["ldx"], a["w"], a["ldw"], a["sw"], a["mode"], a["accum"], a["bias"], a["aq"], a["ldaq"],
+                 a["sa"], a["out"], a["ldo"], a["M"], a["N"], a["K"], a["ws"], NULL)
+    assert call(M=-1) == INVALID and "negative" in _err(lib)
+    assert call(N=-1) == INVALID
+    assert call(K=0) == INVALID
+    for ld in ("ldx", "ldaq", "ldw"):
+        assert call(**{ld: 63}) == INVALID, ld
+    assert call(ldo=31) == INVALID
+    assert call(mode=3) == INVALID and "mode" in _err(lib)
+    assert call(accum=2) == INVALID
+    for p in ("x", "w", "sw", "aq", "sa", "out", "ws"):
+        assert call(**{p: NULL}) == INVALID, p
+    assert call(N=0, ldo=0, sa=NULL) == INVALID    # the scale is an output even with N == 0
+    assert call(M=2 ** 31) == UNSUPPORTED
+    assert lib.fp8_linear_workspace_bytes() == lib.fp8_quant_workspace_bytes()
