@@ -12,6 +12,14 @@ Workloads (synthetic, seeded; the models' shapes only -- no checkpoints):
            (1.75 GB, several times the 256 MB Infinity Cache), as successive
            layers of a model would, so they stream from HBM.
   prefill  M = 16 x 1024 = 16384 tokens.  Matrix-core bound: TFLOP/s.
+  skinny   single per-tensor linears at small M: 16 x 4096 -> 4096, and
+           Mistral-7B-shaped GEMMs at M in {1, 3, 7, 13} (and 32, 64) with
+           N not a multiple of 16, weights rotated over >= 1 GiB per shape.
+
+The default run (--workload all) prints the decode line (the headline value
+and roofline) with a "prefill" object (both accumulation modes, per shape)
+and a "skinny" object (per GEMM) added, so one line carries both halves of
+the metric.
 
 Each step is captured once into a HIP graph and replayed (as a serving
 loop would); --eager launches every kernel from Python instead.
@@ -40,7 +48,10 @@ from fp8_w8a8_quantized_amd import synth  # noqa: E402
 METRIC = "W8A8 scaled-GEMM TFLOP/s (% FP8 MFMA peak); decode M≤16 GB/s (% HBM peak)"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 matrix throughput, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix throughput, published
 ROTATE_DECODE = 8
+ROTATE_MIN_BYTES = 1 << 30   # skinny GEMMs: weights rotated over at least this many bytes
+PREFILL_M = 16384
 
 
 def quant_bytes(m, k):
@@ -77,15 +88,23 @@ def recorded_traffic(kernel):
         return None
 
 
-def build_layer(m, rotate):
-    """Quantized weights (on the GPU, per channel) and bf16 activations."""
+def build_layer(m, rotate, cfg=2, weights_from=None):
+    """Quantized weights (on the GPU, per channel) and bf16 activations.
+
+    cfg selects the activations' seed stream (2: decode, 3: prefill); the
+    weights are the decode layer's (cfg 2) in both, or the first copy of
+    `weights_from`'s when given (the same four shapes and channelwise scales).
+    """
     lin = []
     for sub, (name, k, n) in enumerate(synth.LLAMA3_8B_LINEARS):
-        w = synth.bf16_bits_to_torch(synth.weights(2, n, k, sub=sub, row_multipliers=True)).cuda()
-        w_q, s_w = fp8.quant_weight(w, per_channel=True)
-        del w
+        if weights_from is not None:
+            w_q, s_w = weights_from[sub]["copies"][0]
+        else:
+            w = synth.bf16_bits_to_torch(synth.weights(2, n, k, sub=sub, row_multipliers=True)).cuda()
+            w_q, s_w = fp8.quant_weight(w, per_channel=True)
+            del w
         copies = [(w_q, s_w)] + [(w_q.clone(), s_w.clone()) for _ in range(rotate - 1)]
-        x = synth.bf16_bits_to_torch(synth.activations(2, m, k, sub=sub, outliers=True)).cuda()
+        x = synth.bf16_bits_to_torch(synth.activations(cfg, m, k, sub=sub, outliers=True)).cuda()
         lin.append(dict(name=name, k=k, n=n, x=x, copies=copies,
                         a_q=torch.empty((m, k), dtype=torch.uint8, device="cuda"),
                         s_a=torch.empty(1, dtype=torch.float32, device="cuda"),
@@ -101,22 +120,164 @@ def run_step(lin, it, ws, accum):
         fp8.scaled_mm(L["a_q"], w_q, L["s_a"], s_w, True, out=L["out"], accum=accum)
 
 
-def cpu_baseline(m, lin_shapes, row_frac=8, budget_s=10.0):
+def time_graph_per_launch(launch, n_launches, replays=3):
+    """Mean time per launch of a graph holding n_launches back-to-back calls
+    made by launch(); HIP events on the stream the launches run on."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / (replays * n_launches)
+
+
+def time_steps(lin, ws, accum, steps, warmup, eager=False):
+    """Wall time per step: each step's launches captured once per weight copy
+    into a HIP graph and replayed (or launched eagerly)."""
+    rotate = len(lin[0]["copies"])
+    for i in range(warmup):
+        run_step(lin, i, ws, accum)
+    torch.cuda.synchronize()
+    if eager:
+        def step_fn(i):
+            run_step(lin, i, ws, accum)
+    else:
+        # one HIP graph per weight copy; the library calls allocate nothing and
+        # never synchronize, so a whole step (8 launches) replays as one graph
+        step_graphs = []
+        for r in range(rotate):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run_step(lin, r, ws, accum)
+            step_graphs.append(g)
+        torch.cuda.synchronize()
+
+        def step_fn(i):
+            step_graphs[i % rotate].replay()
+        for i in range(warmup):
+            step_fn(i)
+        torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step_fn(i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def gemm_times(lin, accum, reps):
+    """Per-launch GEMM time of each linear: a graph of back-to-back GEMM
+    launches over the weight copies (the activation codes and scale from the
+    last step)."""
+    out = []
+    for L in lin:
+        rotate = len(L["copies"])
+
+        def launch(L=L):
+            for _ in range(reps):
+                for (w_q, s_w) in L["copies"]:
+                    fp8.scaled_mm(L["a_q"], w_q, L["s_a"], s_w, True, out=L["out"], accum=accum)
+        out.append(time_graph_per_launch(launch, reps * rotate))
+    return out
+
+
+def bench_prefill_modes(weights_from, args):
+    """The four linears at M = 16384, in both accumulation modes: per-shape
+    GEMM time, TFLOP/s and share of peak, and the whole step (quantization +
+    GEMM for the four linears)."""
+    m = PREFILL_M
+    log(f"building inputs: prefill, M={m}")
+    lin = build_layer(m, 1, cfg=3, weights_from=weights_from)
+    ws = fp8.new_workspace()
+    flops = [2 * m * L["k"] * L["n"] for L in lin]
+    res = {"M": m, "workload": "llama3-8b prefill linears (qkv, o, gate_up, down), M=16384 (16 x 1024 tokens), "
+                               "channelwise weight scales, dynamic per-tensor activation scale",
+           "peak_tflops": {"fp8": FP8_PEAK_TFLOPS, "bf16": BF16_PEAK_TFLOPS}, "modes": {}}
+    for accum in ("fp32", "fp8"):
+        step_ms = time_steps(lin, ws, accum, steps=args.prefill_steps, warmup=2)
+        per = gemm_times(lin, accum, reps=3)
+        gemm_tflops = sum(flops) / sum(per) / 1e12
+        r = {"kernel": f"gemm_mfma_kernel<{'true' if accum == 'fp32' else 'false'}, true, 0, 0>",
+             "sums": ("bf16 matrix cores on exactly converted e4m3 values (fp32-class sums; the default)"
+                      if accum == "fp32" else "fp8 matrix cores (13-bit sums inside each group of 8 products)"),
+             "per_shape_us": {L["name"]: round(t * 1e6, 2) for L, t in zip(lin, per)},
+             "per_shape_tflops": {L["name"]: round(f / t / 1e12, 1) for L, f, t in zip(lin, flops, per)},
+             "gemm_tflops": round(gemm_tflops, 1),
+             "frac_fp8_peak": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
+             "step_ms": round(step_ms, 4),
+             "step_tflops": round(sum(flops) / (step_ms * 1e-3) / 1e12, 1)}
+        if accum == "fp32":
+            r["frac_bf16_peak"] = round(gemm_tflops / BF16_PEAK_TFLOPS, 4)
+        r["traffic"] = recorded_traffic(r["kernel"])
+        res["modes"][accum] = r
+        log(f"prefill {accum}: GEMM {gemm_tflops:.0f} TFLOP/s, step {step_ms:.3f} ms")
+    del lin
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_skinny(args):
+    """Single per-tensor linears at small M (GEMM only; activations quantized
+    once): 16 x 4096 -> 4096, and Mistral-7B-shaped GEMMs at M in {1, 3, 7,
+    13} with N in {4096, 14336, 4100, 1030, 6144} (K = 4096) and 14336 -> 4096,
+    plus M = 32 and 64 on the same shapes.  Each shape's weight rotates over
+    copies totalling at least 1 GiB, so it streams from HBM."""
+    log("building inputs: skinny GEMMs")
+    pool = {}
+    for j, (k, n) in enumerate(synth.MISTRAL_7B_KN):
+        w = synth.bf16_bits_to_torch(synth.weights(4, n, k, sub=j)).cuda()
+        w_q, s_w = fp8.quant_weight(w, per_channel=False)
+        del w
+        copies = -(-ROTATE_MIN_BYTES // (n * k))
+        pool[(k, n)] = [(w_q, s_w)] + [(w_q.clone(), s_w) for _ in range(copies - 1)]
+    torch.cuda.synchronize()
+    cases = [(1, 16, 4096, 4096, "single linear 16x4096x4096, per tensor")]
+    cases += [(4, m, k, n, "mistral-7b shapes, per tensor") for m in synth.MISTRAL_7B_SKINNY_M
+              for (k, n) in synth.MISTRAL_7B_KN]
+    cases += [(4, m, k, n, "mistral-7b shapes at larger M, per tensor") for m in (32, 64)
+              for (k, n) in synth.MISTRAL_7B_KN]
+    rows = []
+    for (cfg, m, k, n, what) in cases:
+        copies = pool[(k, n)]
+        x = synth.bf16_bits_to_torch(synth.activations(cfg, m, k, sub=1000 + m)).cuda()
+        a_q, s_a = fp8.quant_dynamic(x)
+        out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+
+        def launch(copies=copies, a_q=a_q, s_a=s_a, out=out):
+            for (w_q, s_w) in copies:
+                fp8.scaled_mm(a_q, w_q, s_a, s_w, False, out=out)
+        t = time_graph_per_launch(launch, len(copies))
+        b = gemm_bytes(m, k, n, per_channel=False)
+        rows.append({"M": m, "K": k, "N": n, "what": what, "us": round(t * 1e6, 2),
+                     "GBps": round(b / t / 1e9, 1), "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes": b, "rotation_copies": len(copies)})
+    del pool
+    torch.cuda.empty_cache()
+    hbm = [r for r in rows if r["M"] <= 16]
+    return {"workload": "per-tensor W8A8 GEMMs at small M (decode), weights rotated over >= 1 GiB per shape; "
+                        "bytes = N*K + M*K + 2*M*N + 8",
+            "gemms": rows,
+            "mean_frac_hbm_m_le_16": round(float(np.mean([r["frac_hbm"] for r in hbm])), 4)}
+
+
+def cpu_baseline(m, lin_shapes, row_frac=8, budget_s=8.0, threads=None):
     """Time the CPU oracle on a bounded sample of the same workload.
 
     Sample: each of the four linears restricted to its first N / row_frac
     output channels (same K, same M, same generators), quantized once
     (load-time work, untimed); then oracle steps (dynamic activation
     quantization + exact GEMM + epilogue for the four linears) repeat until
-    about budget_s of timed work.  Returns (bytes, flops, seconds, threads,
-    description) for the timed steps.
+    about budget_s of timed work.  threads: the BLAS thread count (None:
+    the library's default, all visible cores).  Returns (bytes, flops,
+    seconds, threads, description) for the timed steps.
     """
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    from threadpoolctl import threadpool_info, threadpool_limits
     prepared = []
     for sub, (name, k, n) in enumerate(lin_shapes):
         ns = max(1, n // row_frac)
@@ -125,18 +286,20 @@ def cpu_baseline(m, lin_shapes, row_frac=8, budget_s=10.0):
         w = synth.weights(2, ns, k, sub=sub, row_multipliers=True)
         wq, sw = oracle.quant_weight(w, per_channel=True)
         prepared.append((name, k, ns, x, wq, sw))
-    done_bytes = done_flops = 0
-    timed = 0.0
-    steps = 0
-    while steps == 0 or timed < budget_s:
-        for (name, k, ns, x, wq, sw) in prepared:
-            t0 = time.perf_counter()
-            aq, sa = oracle.quant_dynamic(x)
-            oracle.scaled_mm(aq, wq, sa, sw, True)
-            timed += time.perf_counter() - t0
-            done_bytes += quant_bytes(m, k) + gemm_bytes(m, k, ns)
-            done_flops += 2 * m * k * ns
-        steps += 1
+    with threadpool_limits(limits=threads):
+        used = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        done_bytes = done_flops = 0
+        timed = 0.0
+        steps = 0
+        while steps == 0 or timed < budget_s:
+            for (name, k, ns, x, wq, sw) in prepared:
+                t0 = time.perf_counter()
+                aq, sa = oracle.quant_dynamic(x)
+                oracle.scaled_mm(aq, wq, sa, sw, True)
+                timed += time.perf_counter() - t0
+                done_bytes += quant_bytes(m, k) + gemm_bytes(m, k, ns)
+                done_flops += 2 * m * k * ns
+            steps += 1
     cpu = "unknown CPU"
     try:
         with open("/proc/cpuinfo") as f:
@@ -145,8 +308,25 @@ def cpu_baseline(m, lin_shapes, row_frac=8, budget_s=10.0):
         pass
     desc = (f"{steps} oracle steps over the 4 linears at M={m} with N/{row_frac} output channels each "
             f"({timed:.1f} s timed; weight quantization untimed; element-wise NumPy on 1 thread, "
-            f"fp64 BLAS matmul on {threads}; {cpu}, {os.cpu_count()} logical CPUs visible)")
-    return done_bytes, done_flops, timed, threads, desc
+            f"fp64 BLAS matmul on {used} thread(s); {cpu}, {os.cpu_count()} logical CPUs visible)")
+    return done_bytes, done_flops, timed, used, desc
+
+
+def cpu_baselines(decode):
+    """The oracle on all cores (the reported cpu_baseline) and on 1 thread."""
+    shapes = synth.LLAMA3_8B_LINEARS
+    cm = 16 if decode else 64          # prefill sample: 64 of the 16384 rows
+    res = []
+    for threads in (None, 1):
+        nbytes, nflops, secs, used, desc = cpu_baseline(cm, shapes, threads=threads)
+        if decode:
+            cv, cu = nbytes / secs / 1e9, "GB/s"
+        else:
+            cv, cu = nflops / secs / 1e12, "TFLOP/s"
+        res.append({"value": round(cv, 4), "unit": cu, "cores": used, "kind": "oracle", "sample": desc})
+    all_cores, one = res
+    all_cores["one_thread"] = one
+    return all_cores
 
 
 def run_chain(args):
@@ -228,11 +408,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", choices=["decode", "prefill", "chain"], default="decode",
-                    help="chain: the 32-layer Llama-3-8B-shaped stack, 16 x 1024-token prefill, then decode steps "
-                         "at M=16 (--steps of them, default 512)")
+    ap.add_argument("--workload", choices=["all", "decode", "prefill", "skinny", "chain"], default="all",
+                    help="all (default): the decode line with prefill (both accumulation modes) and skinny "
+                         "objects added; decode / prefill: that workload alone as the headline; skinny: the "
+                         "small-M per-tensor GEMMs alone; chain: the 32-layer Llama-3-8B-shaped stack, "
+                         "16 x 1024-token prefill, then decode steps at M=16 (--steps of them, default 512)")
     ap.add_argument("--accum", choices=["fp32", "fp8"], default="fp32",
-                    help="GEMM accumulation: fp32-class sums (default) or the fp8 matrix cores (M > 16)")
+                    help="GEMM accumulation of the decode / prefill / chain workloads: fp32-class sums (default) "
+                         "or the fp8 matrix cores (M > 64)")
+    ap.add_argument("--prefill-steps", type=int, default=5, help="timed prefill steps per mode in the default run")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from Python instead of replaying captured HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -247,67 +431,29 @@ def main():
         sys.exit(2)
     if args.workload == "chain":
         return run_chain(args)
-    decode = args.workload == "decode"
-    m = 16 if decode else 16384
+    torch.cuda.set_device(0)
+    if args.workload == "skinny":
+        line = {"metric": METRIC + " -- small-M per-tensor GEMMs", "unit": "GB/s", "n_gpus": 1,
+                "higher_is_better": True, "data": "synthetic", "skinny": bench_skinny(args)}
+        line["value"] = round(float(np.mean([r["GBps"] for r in line["skinny"]["gemms"] if r["M"] <= 16])), 1)
+        print(json.dumps(line), flush=True)
+        return
+    decode = args.workload in ("all", "decode")
+    m = 16 if decode else PREFILL_M
     steps = args.steps if args.steps is not None else (200 if decode else 20)
     warmup = args.warmup if args.warmup is not None else (20 if decode else 3)
     rotate = ROTATE_DECODE if decode else 1
-    torch.cuda.set_device(0)
 
-    log(f"building inputs: {args.workload}, M={m}, rotate={rotate}")
-    lin = build_layer(m, rotate)
+    log(f"building inputs: {'decode' if decode else 'prefill'}, M={m}, rotate={rotate}")
+    lin = build_layer(m, rotate, cfg=2 if decode else 3)
     ws = fp8.new_workspace()
-    for i in range(warmup):
-        run_step(lin, i, ws, args.accum)
-    torch.cuda.synchronize()
-
-    if args.eager:
-        def step_fn(i):
-            run_step(lin, i, ws, args.accum)
-    else:
-        # one HIP graph per weight copy; the library calls allocate nothing and
-        # never synchronize, so a whole step (8 launches) replays as one graph
-        step_graphs = []
-        for r in range(rotate):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                run_step(lin, r, ws, args.accum)
-            step_graphs.append(g)
-        torch.cuda.synchronize()
-
-        def step_fn(i):
-            step_graphs[i % rotate].replay()
-        for i in range(warmup):
-            step_fn(i)
-        torch.cuda.synchronize()
-
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step_fn(i)
-    torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+    ms_per_step = time_steps(lin, ws, args.accum, steps, warmup, eager=args.eager)
 
     # Per-launch GEMM time: for each linear, a graph of back-to-back GEMM
     # launches over the weight copies, bracketed by HIP events on the stream
     # the launches run on; mean time per launch.
     reps = max(1, 16 // rotate) if decode else 3
-    per_shape_s = []
-    for L in lin:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for rep in range(reps):
-                for r in range(rotate):
-                    w_q, s_w = L["copies"][r]
-                    fp8.scaled_mm(L["a_q"], w_q, L["s_a"], s_w, True, out=L["out"], accum=args.accum)
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(3):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        per_shape_s.append(e0.elapsed_time(e1) * 1e-3 / (3 * reps * rotate))
+    per_shape_s = gemm_times(lin, args.accum, reps)
 
     if args.copy_calibration_mib > 0:
         nb = args.copy_calibration_mib << 20
@@ -358,19 +504,16 @@ def main():
                    "launch": "eager" if args.eager else "hip_graph"},
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
+    if args.workload == "all":
+        line["prefill"] = bench_prefill_modes(lin, args)
         del lin
         torch.cuda.empty_cache()
-        shapes = synth.LLAMA3_8B_LINEARS
-        cm = m if decode else 64          # prefill sample: 64 of the 16384 rows
-        nbytes, nflops, secs, threads, desc = cpu_baseline(cm, shapes)
-        if decode:
-            cv, cu = nbytes / secs / 1e9, "GB/s"
-        else:
-            cv, cu = nflops / secs / 1e12, "TFLOP/s"
-        line["cpu_baseline"] = {
-            "value": round(cv, 4), "unit": cu, "cores": threads, "kind": "oracle",
-            "sample": desc}
+        line["skinny"] = bench_skinny(args)
+    else:
+        del lin
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baselines(decode)
     print(json.dumps(line), flush=True)
 
 

@@ -32,7 +32,7 @@ SIGNATURES = {
     "fp8_quant_dynamic": (_I, [_P, _I64, _I64, _I64, _P, _I64, _P, _P, _P]),
     "fp8_quant_static": (_I, [_P, _I64, _I64, _I64, _P, _P, _I64, _P]),
     "fp8_quant_dynamic_per_row": (_I, [_P, _I64, _I64, _I64, _P, _I64, _P, _P]),
-    "fp8_scaled_mm": (_I, [_P, _I64, _P, _I64, _P, _P, _I, _I, _P, _P, _I64, _I64, _I64, _I64, _P]),
+    "fp8_scaled_mm": (_I, [_P, _I64, _P, _I64, _P, _P, _I, _P, _P, _I64, _I64, _I64, _I64, _P]),
     "fp8_quant_dynamic_fmt": (_I, [_P, _I64, _I64, _I64, _I, _P, _I64, _P, _P, _P]),
     "fp8_quant_static_fmt": (_I, [_P, _I64, _I64, _I64, _I, _P, _P, _I64, _P]),
     "fp8_quant_dynamic_per_row_fmt": (_I, [_P, _I64, _I64, _I64, _I, _P, _I64, _P, _P]),
@@ -79,13 +79,59 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _mat(t, name, dtype):
-    if not t.is_cuda:
+# ---------------------------------------------------------------- validation
+# Every tensor is checked (device, dtype, shape or element count, strides)
+# before any library call: the kernels trust the sizes they are given, so a
+# short scale vector or a host tensor would otherwise become an out-of-range
+# device access.
+
+def _on_gpu(t):
+    return t.is_cuda
+
+
+def _device(t, name, device):
+    if not _on_gpu(t):
         raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _mat(t, name, dtype, shape=None, device=None):
+    """A 2-D tensor of `dtype` with unit column stride (any row pitch >= cols)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    _device(t, name, device)
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if t.dim() != 2 or (t.size(1) > 1 and t.stride(1) != 1) or t.stride(0) < max(t.size(1), 1):
-        raise ValueError(f"{name} must be 2-D with unit column stride")
+        raise ValueError(f"{name} must be 2-D with unit column stride and row pitch >= its columns")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _vec(t, name, dtype, n, device):
+    """A contiguous tensor of exactly n elements of `dtype` on `device`."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    _device(t, name, device)
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.numel() != n:
+        raise ValueError(f"{name} must have {n} element(s), got {t.numel()}")
+    if n > 1 and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _workspace(t, name, nbytes, device):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    _device(t, name, device)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {nbytes}")
     return t
 
 
@@ -104,6 +150,18 @@ def new_workspace(device=None):
 FORMAT = {"e4m3": 0, "e5m2": 1}
 
 
+def _fmt(fmt):
+    if fmt not in FORMAT:
+        raise ValueError(f"unknown fp8 format {fmt!r} (expected one of {sorted(FORMAT)})")
+    return FORMAT[fmt]
+
+
+def _accum(accum):
+    if accum not in ACCUM:
+        raise ValueError(f"unknown accumulation mode {accum!r} (expected one of {sorted(ACCUM)})")
+    return ACCUM[accum]
+
+
 def quant_dynamic(x, workspace=None, q=None, scale=None, fmt="e4m3"):
     """Dynamic per-tensor quantization of bf16 x [rows, cols] into fmt codes.
 
@@ -111,11 +169,16 @@ def quant_dynamic(x, workspace=None, q=None, scale=None, fmt="e4m3"):
     device.
     """
     _mat(x, "x", torch.bfloat16)
+    dev = x.device
     rows, cols = x.shape
-    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if q is None else q
-    scale = torch.empty(1, dtype=torch.float32, device=x.device) if scale is None else scale
-    workspace = new_workspace(x.device) if workspace is None else workspace
-    _check(lib().fp8_quant_dynamic_fmt(_ptr(x), rows, cols, x.stride(0), FORMAT[fmt], _ptr(q), q.stride(0),
+    f = _fmt(fmt)
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=dev) if q is None else q
+    scale = torch.empty(1, dtype=torch.float32, device=dev) if scale is None else scale
+    _mat(q, "q", torch.uint8, (rows, cols), dev)
+    _vec(scale, "scale", torch.float32, 1, dev)
+    workspace = new_workspace(dev) if workspace is None else workspace
+    _workspace(workspace, "workspace", workspace_bytes(), dev)
+    _check(lib().fp8_quant_dynamic_fmt(_ptr(x), rows, cols, x.stride(0), f, _ptr(q), q.stride(0),
                                        _ptr(scale), _ptr(workspace), _stream()), "fp8_quant_dynamic")
     return q, scale
 
@@ -123,9 +186,13 @@ def quant_dynamic(x, workspace=None, q=None, scale=None, fmt="e4m3"):
 def quant_static(x, scale, q=None, fmt="e4m3"):
     """Quantize bf16 x with a given device float32 scale; returns q uint8."""
     _mat(x, "x", torch.bfloat16)
+    dev = x.device
     rows, cols = x.shape
-    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if q is None else q
-    _check(lib().fp8_quant_static_fmt(_ptr(x), rows, cols, x.stride(0), FORMAT[fmt], _ptr(scale), _ptr(q),
+    f = _fmt(fmt)
+    _vec(scale, "scale", torch.float32, 1, dev)
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=dev) if q is None else q
+    _mat(q, "q", torch.uint8, (rows, cols), dev)
+    _check(lib().fp8_quant_static_fmt(_ptr(x), rows, cols, x.stride(0), f, _ptr(scale), _ptr(q),
                                       q.stride(0), _stream()), "fp8_quant_static")
     return q
 
@@ -133,10 +200,14 @@ def quant_static(x, scale, q=None, fmt="e4m3"):
 def quant_dynamic_per_row(x, q=None, scales=None, fmt="e4m3"):
     """One scale per row (channelwise weight quantization): (q, scales [rows])."""
     _mat(x, "x", torch.bfloat16)
+    dev = x.device
     rows, cols = x.shape
-    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if q is None else q
-    scales = torch.empty(rows, dtype=torch.float32, device=x.device) if scales is None else scales
-    _check(lib().fp8_quant_dynamic_per_row_fmt(_ptr(x), rows, cols, x.stride(0), FORMAT[fmt], _ptr(q), q.stride(0),
+    f = _fmt(fmt)
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=dev) if q is None else q
+    scales = torch.empty(rows, dtype=torch.float32, device=dev) if scales is None else scales
+    _mat(q, "q", torch.uint8, (rows, cols), dev)
+    _vec(scales, "scales", torch.float32, rows, dev)
+    _check(lib().fp8_quant_dynamic_per_row_fmt(_ptr(x), rows, cols, x.stride(0), f, _ptr(q), q.stride(0),
                                                _ptr(scales), _stream()), "fp8_quant_dynamic_per_row")
     return q, scales
 
@@ -148,25 +219,43 @@ def quant_weight(w, per_channel, fmt="e4m3"):
     return quant_dynamic(w, fmt=fmt)
 
 
+def _gemm_operands(a_q, w_q, s_a, s_w, per_channel, bias, out):
+    """Validate the scaled GEMM's tensors; returns (M, N, K, out)."""
+    _mat(a_q, "a_q", torch.uint8)
+    dev = a_q.device
+    _mat(w_q, "w_q", torch.uint8, device=dev)
+    M, K = a_q.shape
+    N, K2 = w_q.shape
+    if K != K2:
+        raise ValueError(f"K mismatch: a_q has {K}, w_q has {K2}")
+    _vec(s_a, "s_a", torch.float32, 1, dev)
+    _vec(s_w, "s_w", torch.float32, N if per_channel else 1, dev)
+    if bias is not None:
+        _vec(bias, "bias", torch.bfloat16, N, dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if out is None else out
+    _mat(out, "out", torch.bfloat16, (M, N), dev)
+    return M, N, K, out
+
+
 def scaled_mm(a_q, w_q, s_a, s_w, per_channel, bias=None, out=None, accum="fp32", fmt_a="e4m3", fmt_w="e4m3"):
     """out[M, N] = bf16((A_q @ W_q^T) * s_a * s_w (+ bias)); W_q is [N, K].
 
     accum: "fp32" (fp32-class sums, default) or "fp8" (fp8 matrix cores for
     M > 64: twice the rate, 13-bit sums inside each group of 8 products).
-    fmt_a / fmt_w: "e4m3" or "e5m2" codes.
+    fmt_a / fmt_w: "e4m3" or "e5m2" codes.  The default (e4m3 codes, fp32
+    sums) is the library's fp8_scaled_mm; other choices go through
+    fp8_scaled_mm_fmt.
     """
-    _mat(a_q, "a_q", torch.uint8)
-    _mat(w_q, "w_q", torch.uint8)
-    M, K = a_q.shape
-    N, K2 = w_q.shape
-    if K != K2:
-        raise ValueError(f"K mismatch: a_q has {K}, w_q has {K2}")
-    out = torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device) if out is None else out
+    fa, fw, acc = _fmt(fmt_a), _fmt(fmt_w), _accum(accum)
+    M, N, K, out = _gemm_operands(a_q, w_q, s_a, s_w, per_channel, bias, out)
     mode = FP8_SCALE_PER_CHANNEL if per_channel else FP8_SCALE_PER_TENSOR
-    _check(lib().fp8_scaled_mm_fmt(_ptr(a_q), a_q.stride(0), FORMAT[fmt_a], _ptr(w_q), w_q.stride(0),
-                                   FORMAT[fmt_w], _ptr(s_a), _ptr(s_w), mode, ACCUM[accum], _ptr(bias), _ptr(out),
-                                   out.stride(0), M, N, K, _stream()),
-           "fp8_scaled_mm")
+    if fa == 0 and fw == 0 and acc == FP8_ACCUM_FP32:
+        _check(lib().fp8_scaled_mm(_ptr(a_q), a_q.stride(0), _ptr(w_q), w_q.stride(0), _ptr(s_a), _ptr(s_w), mode,
+                                   _ptr(bias), _ptr(out), out.stride(0), M, N, K, _stream()), "fp8_scaled_mm")
+    else:
+        _check(lib().fp8_scaled_mm_fmt(_ptr(a_q), a_q.stride(0), fa, _ptr(w_q), w_q.stride(0), fw, _ptr(s_a),
+                                       _ptr(s_w), mode, acc, _ptr(bias), _ptr(out), out.stride(0), M, N, K,
+                                       _stream()), "fp8_scaled_mm_fmt")
     return out
 
 
@@ -187,19 +276,18 @@ def linear_dynamic(x, w_q, s_w, per_channel, bias=None, workspace=None, a_q=None
 
     Returns (out [M, N] bf16, a_q [M, K] uint8, s_a [1] float32).
     """
+    acc = _accum(accum)
     _mat(x, "x", torch.bfloat16)
-    _mat(w_q, "w_q", torch.uint8)
-    M, K = x.shape
-    N, K2 = w_q.shape
-    if K != K2:
-        raise ValueError(f"K mismatch: x has {K}, w_q has {K2}")
     dev = x.device
+    M, K = x.shape
     a_q = torch.empty((M, K), dtype=torch.uint8, device=dev) if a_q is None else a_q
     s_a = torch.empty(1, dtype=torch.float32, device=dev) if s_a is None else s_a
-    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if out is None else out
+    _mat(a_q, "a_q", torch.uint8, (M, K), dev)
+    M, N, K, out = _gemm_operands(a_q, w_q, s_a, s_w, per_channel, bias, out)
     workspace = new_linear_workspace(dev) if workspace is None else workspace
+    _workspace(workspace, "workspace", linear_workspace_bytes(), dev)
     mode = FP8_SCALE_PER_CHANNEL if per_channel else FP8_SCALE_PER_TENSOR
-    _check(lib().fp8_linear_dynamic(_ptr(x), x.stride(0), _ptr(w_q), w_q.stride(0), _ptr(s_w), mode, ACCUM[accum],
+    _check(lib().fp8_linear_dynamic(_ptr(x), x.stride(0), _ptr(w_q), w_q.stride(0), _ptr(s_w), mode, acc,
                                     _ptr(bias), _ptr(a_q), a_q.stride(0), _ptr(s_a), _ptr(out), out.stride(0),
                                     M, N, K, _ptr(workspace), _stream()),
            "fp8_linear_dynamic")
@@ -233,15 +321,20 @@ def add_rmsnorm_quant(h, delta=None, h_out=None, eps=1e-5, y_out=None, q=None, s
     receives the normalized bf16 values that were quantized.
     """
     _mat(h, "h", torch.bfloat16)
+    dev = h.device
     rows, cols = h.shape
     if delta is not None:
-        _mat(delta, "delta", torch.bfloat16)
-        h_out = torch.empty_like(h) if h_out is None else _mat(h_out, "h_out", torch.bfloat16)
+        _mat(delta, "delta", torch.bfloat16, (rows, cols), dev)
+        h_out = torch.empty_like(h) if h_out is None else h_out
+        _mat(h_out, "h_out", torch.bfloat16, (rows, cols), dev)
     if y_out is not None:
-        _mat(y_out, "y_out", torch.bfloat16)
-    q = torch.empty((rows, cols), dtype=torch.uint8, device=h.device) if q is None else q
-    scale = torch.empty(1, dtype=torch.float32, device=h.device) if scale is None else scale
-    workspace = norm_workspace(rows, h.device) if workspace is None else workspace
+        _mat(y_out, "y_out", torch.bfloat16, (rows, cols), dev)
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=dev) if q is None else q
+    scale = torch.empty(1, dtype=torch.float32, device=dev) if scale is None else scale
+    _mat(q, "q", torch.uint8, (rows, cols), dev)
+    _vec(scale, "scale", torch.float32, 1, dev)
+    workspace = norm_workspace(rows, dev) if workspace is None else workspace
+    _workspace(workspace, "workspace", int(lib().fp8_norm_quant_workspace_bytes(rows)), dev)
     _check(lib().fp8_add_rmsnorm_quant_dynamic(
         _ptr(h), h.stride(0), _ptr(delta), delta.stride(0) if delta is not None else 0,
         _ptr(h_out if delta is not None else None), h_out.stride(0) if delta is not None else 0,
@@ -254,15 +347,19 @@ def silu_mul_quant(gu, y_out=None, q=None, scale=None, workspace=None):
     """silu(gate) * up of a fused gate_up output [rows, 2 cols] (gate first),
     quantized with a dynamic per-tensor scale.  Returns (q, scale, y_out)."""
     _mat(gu, "gu", torch.bfloat16)
+    dev = gu.device
     rows, two_cols = gu.shape
     if two_cols % 2:
         raise ValueError("gu must have an even number of columns (gate | up)")
     cols = two_cols // 2
     if y_out is not None:
-        _mat(y_out, "y_out", torch.bfloat16)
-    q = torch.empty((rows, cols), dtype=torch.uint8, device=gu.device) if q is None else q
-    scale = torch.empty(1, dtype=torch.float32, device=gu.device) if scale is None else scale
-    workspace = new_workspace(gu.device) if workspace is None else workspace
+        _mat(y_out, "y_out", torch.bfloat16, (rows, cols), dev)
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=dev) if q is None else q
+    scale = torch.empty(1, dtype=torch.float32, device=dev) if scale is None else scale
+    _mat(q, "q", torch.uint8, (rows, cols), dev)
+    _vec(scale, "scale", torch.float32, 1, dev)
+    workspace = new_workspace(dev) if workspace is None else workspace
+    _workspace(workspace, "workspace", workspace_bytes(), dev)
     _check(lib().fp8_silu_mul_quant_dynamic(_ptr(gu), gu.stride(0), rows, cols, _ptr(y_out),
                                             y_out.stride(0) if y_out is not None else 0, _ptr(q), q.stride(0),
                                             _ptr(scale), _ptr(workspace), _stream()), "fp8_silu_mul_quant_dynamic")

@@ -56,7 +56,7 @@ size_t fp8_quant_workspace_bytes(void) { return fp8w8a8::quant_workspace_bytes()
 const char* fp8_last_error(void) { return g_err; }
 
 fp8_status fp8_quant_dynamic_fmt(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, fp8_format fmt,
-                                 uint8_t* q, int64_t ld_q, float* scale_out, void* workspace, void* stream) {
+                                 uint8_t* q, int64_t ld_q, float* scale_out, void* workspace, hipStream_t stream) {
   const char* fn = "fp8_quant_dynamic";
   fp8_status st = check_quant(fn, x_bf16, rows, cols, ld_x, q, ld_q);
   if (st == FP8_OK) st = check_fmt(fn, fmt);
@@ -64,46 +64,46 @@ fp8_status fp8_quant_dynamic_fmt(const uint16_t* x_bf16, int64_t rows, int64_t c
   if (scale_out == nullptr) return fail(FP8_ERR_INVALID_ARG, "%s: null scale_out", fn);
   if (rows > 0 && cols > 0 && workspace == nullptr) return fail(FP8_ERR_INVALID_ARG, "%s: null workspace", fn);
   return hip_status(fp8w8a8::launch_quant_dynamic(x_bf16, rows, cols, ld_x, (int)fmt, q, ld_q, scale_out, workspace,
-                                                  static_cast<hipStream_t>(stream)),
+                                                  stream),
                     fn);
 }
 
 fp8_status fp8_quant_dynamic(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q_e4m3,
-                             int64_t ld_q, float* scale_out, void* workspace, void* stream) {
+                             int64_t ld_q, float* scale_out, void* workspace, hipStream_t stream) {
   return fp8_quant_dynamic_fmt(x_bf16, rows, cols, ld_x, FP8_FORMAT_E4M3, q_e4m3, ld_q, scale_out, workspace, stream);
 }
 
 fp8_status fp8_quant_static_fmt(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, fp8_format fmt,
-                                const float* scale, uint8_t* q, int64_t ld_q, void* stream) {
+                                const float* scale, uint8_t* q, int64_t ld_q, hipStream_t stream) {
   const char* fn = "fp8_quant_static";
   fp8_status st = check_quant(fn, x_bf16, rows, cols, ld_x, q, ld_q);
   if (st == FP8_OK) st = check_fmt(fn, fmt);
   if (st != FP8_OK) return st;
   if (scale == nullptr) return fail(FP8_ERR_INVALID_ARG, "%s: null scale", fn);
   return hip_status(fp8w8a8::launch_quant_static(x_bf16, rows, cols, ld_x, (int)fmt, scale, q, ld_q,
-                                                 static_cast<hipStream_t>(stream)),
+                                                 stream),
                     fn);
 }
 
 fp8_status fp8_quant_static(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, const float* scale,
-                            uint8_t* q_e4m3, int64_t ld_q, void* stream) {
+                            uint8_t* q_e4m3, int64_t ld_q, hipStream_t stream) {
   return fp8_quant_static_fmt(x_bf16, rows, cols, ld_x, FP8_FORMAT_E4M3, scale, q_e4m3, ld_q, stream);
 }
 
 fp8_status fp8_quant_dynamic_per_row_fmt(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
-                                         fp8_format fmt, uint8_t* q, int64_t ld_q, float* scales_out, void* stream) {
+                                         fp8_format fmt, uint8_t* q, int64_t ld_q, float* scales_out, hipStream_t stream) {
   const char* fn = "fp8_quant_dynamic_per_row";
   fp8_status st = check_quant(fn, x_bf16, rows, cols, ld_x, q, ld_q);
   if (st == FP8_OK) st = check_fmt(fn, fmt);
   if (st != FP8_OK) return st;
   if (rows > 0 && scales_out == nullptr) return fail(FP8_ERR_INVALID_ARG, "%s: null scales_out", fn);
   return hip_status(fp8w8a8::launch_quant_per_row(x_bf16, rows, cols, ld_x, (int)fmt, q, ld_q, scales_out,
-                                                  static_cast<hipStream_t>(stream)),
+                                                  stream),
                     fn);
 }
 
 fp8_status fp8_quant_dynamic_per_row(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
-                                     uint8_t* q_e4m3, int64_t ld_q, float* scales_out, void* stream) {
+                                     uint8_t* q_e4m3, int64_t ld_q, float* scales_out, hipStream_t stream) {
   return fp8_quant_dynamic_per_row_fmt(x_bf16, rows, cols, ld_x, FP8_FORMAT_E4M3, q_e4m3, ld_q, scales_out, stream);
 }
 
@@ -115,7 +115,7 @@ fp8_status fp8_add_rmsnorm_quant_dynamic(const uint16_t* h_bf16, int64_t ld_h, c
                                          int64_t ld_delta, uint16_t* h_out_bf16, int64_t ld_h_out, int64_t rows,
                                          int64_t cols, float eps, uint16_t* y_out_bf16, int64_t ld_y,
                                          uint8_t* q_e4m3, int64_t ld_q, float* scale_out, void* workspace,
-                                         void* stream) {
+                                         hipStream_t stream) {
   const char* fn = "fp8_add_rmsnorm_quant_dynamic";
   fp8_status st = check_quant(fn, h_bf16, rows, cols, ld_h, q_e4m3, ld_q);
   if (st != FP8_OK) return st;
@@ -132,13 +132,13 @@ fp8_status fp8_add_rmsnorm_quant_dynamic(const uint16_t* h_bf16, int64_t ld_h, c
   if (rows >= (1ll << 31)) return fail(FP8_ERR_UNSUPPORTED, "%s: too many rows", fn);
   return hip_status(fp8w8a8::launch_add_rmsnorm_quant(h_bf16, ld_h, delta_bf16, ld_delta, h_out_bf16, ld_h_out, rows,
                                                       cols, eps, y_out_bf16, ld_y, q_e4m3, ld_q, scale_out, workspace,
-                                                      static_cast<hipStream_t>(stream)),
+                                                      stream),
                     fn);
 }
 
 fp8_status fp8_silu_mul_quant_dynamic(const uint16_t* gu_bf16, int64_t ld_gu, int64_t rows, int64_t cols,
                                       uint16_t* y_out_bf16, int64_t ld_y, uint8_t* q_e4m3, int64_t ld_q,
-                                      float* scale_out, void* workspace, void* stream) {
+                                      float* scale_out, void* workspace, hipStream_t stream) {
   const char* fn = "fp8_silu_mul_quant_dynamic";
   fp8_status st = check_quant(fn, gu_bf16, rows, cols, ld_gu, q_e4m3, ld_q);
   if (st != FP8_OK) return st;
@@ -148,14 +148,14 @@ fp8_status fp8_silu_mul_quant_dynamic(const uint16_t* gu_bf16, int64_t ld_gu, in
   if (work && workspace == nullptr) return fail(FP8_ERR_INVALID_ARG, "%s: null workspace", fn);
   if (work && y_out_bf16 != nullptr && ld_y < cols) return fail(FP8_ERR_INVALID_ARG, "%s: ld_y smaller than cols", fn);
   return hip_status(fp8w8a8::launch_silu_mul_quant(gu_bf16, ld_gu, rows, cols, y_out_bf16, ld_y, q_e4m3, ld_q,
-                                                   scale_out, workspace, static_cast<hipStream_t>(stream)),
+                                                   scale_out, workspace, stream),
                     fn);
 }
 
 fp8_status fp8_scaled_mm_fmt(const uint8_t* a_q, int64_t lda, fp8_format fmt_a, const uint8_t* w_q, int64_t ldw,
                              fp8_format fmt_w, const float* s_a, const float* s_w, fp8_scale_mode mode,
                              fp8_accum_mode accum, const uint16_t* bias_bf16, uint16_t* out_bf16, int64_t ldo,
-                             int64_t M, int64_t N, int64_t K, void* stream) {
+                             int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   const char* fn = "fp8_scaled_mm";
   if (check_fmt(fn, fmt_a) != FP8_OK || check_fmt(fn, fmt_w) != FP8_OK) return FP8_ERR_INVALID_ARG;
   if (M < 0 || N < 0) return fail(FP8_ERR_INVALID_ARG, "%s: negative M or N (M=%lld, N=%lld)", fn,
@@ -180,7 +180,7 @@ fp8_status fp8_scaled_mm_fmt(const uint8_t* a_q, int64_t lda, fp8_format fmt_a, 
   g.per_channel = mode == FP8_SCALE_PER_CHANNEL ? 1 : 0;
   g.fmt_a = (int32_t)fmt_a;
   g.fmt_w = (int32_t)fmt_w;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipStream_t s = stream;
 
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
   if (M > 64 && tiles < (1ll << 31) && fp8w8a8::gemm_mfma_supported(g))
@@ -205,7 +205,7 @@ fp8_status fp8_linear_dynamic(const uint16_t* x_bf16, int64_t ld_x, const uint8_
                               const float* s_w, fp8_scale_mode mode, fp8_accum_mode accum,
                               const uint16_t* bias_bf16, uint8_t* a_q, int64_t ld_aq, float* s_a_out,
                               uint16_t* out_bf16, int64_t ldo, int64_t M, int64_t N, int64_t K, void* workspace,
-                              void* stream) {
+                              hipStream_t stream) {
   const char* fn = "fp8_linear_dynamic";
   if (M < 0 || N < 0) return fail(FP8_ERR_INVALID_ARG, "%s: negative M or N (M=%lld, N=%lld)", fn,
                                   (long long)M, (long long)N);
@@ -225,17 +225,18 @@ fp8_status fp8_linear_dynamic(const uint16_t* x_bf16, int64_t ld_x, const uint8_
     return fail(FP8_ERR_UNSUPPORTED, "%s: problem too large", fn);
   // the quantization, then the GEMM on its codes (nothing to multiply for M == 0 or N == 0)
   fp8_status st = hip_status(fp8w8a8::launch_quant_dynamic(x_bf16, M, K, ld_x, FP8_FORMAT_E4M3, a_q, ld_aq,
-                                                           s_a_out, workspace, static_cast<hipStream_t>(stream)),
+                                                           s_a_out, workspace, stream),
                              fn);
   if (st != FP8_OK || M == 0 || N == 0) return st;
-  return fp8_scaled_mm(a_q, ld_aq, w_q, ldw, s_a_out, s_w, mode, accum, bias_bf16, out_bf16, ldo, M, N, K, stream);
+  return fp8_scaled_mm_fmt(a_q, ld_aq, FP8_FORMAT_E4M3, w_q, ldw, FP8_FORMAT_E4M3, s_a_out, s_w, mode, accum,
+                           bias_bf16, out_bf16, ldo, M, N, K, stream);
 }
 
 fp8_status fp8_scaled_mm(const uint8_t* a_q, int64_t lda, const uint8_t* w_q, int64_t ldw, const float* s_a,
-                         const float* s_w, fp8_scale_mode mode, fp8_accum_mode accum, const uint16_t* bias_bf16,
-                         uint16_t* out_bf16, int64_t ldo, int64_t M, int64_t N, int64_t K, void* stream) {
-  return fp8_scaled_mm_fmt(a_q, lda, FP8_FORMAT_E4M3, w_q, ldw, FP8_FORMAT_E4M3, s_a, s_w, mode, accum, bias_bf16,
-                           out_bf16, ldo, M, N, K, stream);
+                         const float* s_w, fp8_scale_mode mode, const uint16_t* bias_bf16, uint16_t* out_bf16,
+                         int64_t ldo, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  return fp8_scaled_mm_fmt(a_q, lda, FP8_FORMAT_E4M3, w_q, ldw, FP8_FORMAT_E4M3, s_a, s_w, mode, FP8_ACCUM_FP32,
+                           bias_bf16, out_bf16, ldo, M, N, K, stream);
 }
 
 }  // extern "C"

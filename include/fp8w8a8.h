@@ -45,6 +45,11 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* The HIP stream type, declared exactly as the HIP runtime declares it, so
+ * this header needs no HIP include (a repeated identical typedef is valid
+ * C11 and C++). */
+typedef struct ihipStream_t* hipStream_t;
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -62,8 +67,9 @@ typedef enum {
 } fp8_scale_mode;
 
 /*
- * How fp8_scaled_mm sums the products (each product of two e4m3 values is
- * exact in every mode).
+ * How fp8_scaled_mm_fmt and fp8_linear_dynamic sum the products (each
+ * product of two e4m3 values is exact in every mode; fp8_scaled_mm always
+ * sums as FP8_ACCUM_FP32).
  *   FP8_ACCUM_FP32      sums with fp32-class precision: the codes are
  *                       converted to bf16 in registers (exact) and run on the
  *                       bf16 matrix cores.  The default.
@@ -112,7 +118,7 @@ size_t fp8_quant_workspace_bytes(void);
  */
 fp8_status fp8_quant_dynamic(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
                              uint8_t* q_e4m3, int64_t ld_q, float* scale_out,
-                             void* workspace, void* stream);
+                             void* workspace, hipStream_t stream);
 
 /*
  * Quantization with a given per-tensor scale (a calibrated, static
@@ -124,7 +130,7 @@ fp8_status fp8_quant_dynamic(const uint16_t* x_bf16, int64_t rows, int64_t cols,
  * Errors: as fp8_quant_dynamic (no workspace).
  */
 fp8_status fp8_quant_static(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
-                            const float* scale, uint8_t* q_e4m3, int64_t ld_q, void* stream);
+                            const float* scale, uint8_t* q_e4m3, int64_t ld_q, hipStream_t stream);
 
 /*
  * Per-row dynamic quantization: row r gets its own scale from its own amax
@@ -137,40 +143,48 @@ fp8_status fp8_quant_static(const uint16_t* x_bf16, int64_t rows, int64_t cols, 
  */
 fp8_status fp8_quant_dynamic_per_row(const uint16_t* x_bf16, int64_t rows, int64_t cols,
                                      int64_t ld_x, uint8_t* q_e4m3, int64_t ld_q,
-                                     float* scales_out, void* stream);
+                                     float* scales_out, hipStream_t stream);
 
 /*
- * Scaled FP8 GEMM with the rescale epilogue fused into the store:
+ * Scaled FP8 GEMM with the rescale epilogue fused into the store.
+ *
+ * Defined by "Prototype FP8Linear W8A8 runtime quantization" (opening post:
+ * an FP8 W8A8 linear multiplies e4m3fn activations by e4m3fn weights, each
+ * with its own scale) and "[Kernel] Implement fallback for FP8 channelwise
+ * using torch._scaled_mm" (description: a per-output-channel weight scale is
+ * a per-tensor scaled GEMM followed by a rescale of each output column;
+ * s_w[n] does not depend on k, so the rescale factors out of the k-sum and is
+ * applied once per output element, here in the GEMM's store):
  *
  *   out[m, n] = bf16_rne( (sum_k dec(a_q[m, k]) * dec(w_q[n, k]))
  *                         * (s_a[0] * s_w[n or 0]) + bias[n] )
  *
- * Products are exact and summed on the matrix cores as `accum` selects
- * (see fp8_accum_mode); the scale product s_a * s_w is formed in float32 and
- * applied with one fused multiply-add together with the bias.  Per-channel
- * with all s_w[n] equal gives bit-identical output to per-tensor with that
- * value.
+ * Products of two e4m3 values are exact and are summed with fp32-class
+ * precision (FP8_ACCUM_FP32 below); the scale product s_a * s_w is formed in
+ * float32 and applied with one fused multiply-add together with the bias.
+ * Per-channel with all s_w[n] equal gives bit-identical output to
+ * per-tensor with that value.
  *
  *   a_q    [M, K] e4m3fn, row pitch lda >= K          (activations)
  *   w_q    [N, K] e4m3fn, row pitch ldw >= K          (nn.Linear weight;
  *                                                      out = A * W^T)
  *   s_a    1 float (device)                            (activation scale)
  *   s_w    1 float (PER_TENSOR) or N floats (PER_CHANNEL) (device)
- *   accum  FP8_ACCUM_FP32 or FP8_ACCUM_FP8_MFMA
- *   bias   N bf16 values, or NULL for none
+ *   bias   N bf16 values (device), or NULL for none
  *   out    [M, N] bf16, row pitch ldo >= N            (output)
- * M <= 64 runs the skinny (decode) kernel, one 16-row block of M per grid
- * row, which streams the weight once with no padding or repacking; larger M
- * runs the LDS-staged matrix-core GEMM (and layouts it does not take -- rows
- * not 16-byte aligned or K % 16 != 0 -- the skinny kernel).  Any M, N,
- * K >= 1 is accepted.
+ * M <= 64 runs the skinny (decode) kernel, which streams the weight once
+ * with no padding or repacking; larger M runs the LDS-staged matrix-core
+ * GEMM (and layouts it does not take -- rows not 16-byte aligned or
+ * K % 16 != 0 -- the skinny kernel).  Any M, N, K >= 1 is accepted.
  * Errors: INVALID_ARG for null pointers (bias may be NULL), negative M or
- * N, K < 1, lda/ldw < K, ldo < N, or an unknown scale or accumulation mode.
+ * N, K < 1, lda/ldw < K, ldo < N, or an unknown scale mode; UNSUPPORTED for
+ * M or N >= 2^31, K >= 2^30 or pitches >= 2^40.  M == 0 or N == 0 is an
+ * OK no-op.
  */
 fp8_status fp8_scaled_mm(const uint8_t* a_q, int64_t lda, const uint8_t* w_q, int64_t ldw,
                          const float* s_a, const float* s_w, fp8_scale_mode mode,
-                         fp8_accum_mode accum, const uint16_t* bias_bf16, uint16_t* out_bf16,
-                         int64_t ldo, int64_t M, int64_t N, int64_t K, void* stream);
+                         const uint16_t* bias_bf16, uint16_t* out_bf16, int64_t ldo,
+                         int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 /*
  * The whole W8A8 linear in one call: dynamic per-tensor quantization of the
@@ -197,7 +211,7 @@ fp8_status fp8_linear_dynamic(const uint16_t* x_bf16, int64_t ld_x, const uint8_
                               const float* s_w, fp8_scale_mode mode, fp8_accum_mode accum,
                               const uint16_t* bias_bf16, uint8_t* a_q, int64_t ld_aq, float* s_a_out,
                               uint16_t* out_bf16, int64_t ldo, int64_t M, int64_t N, int64_t K,
-                              void* workspace, void* stream);
+                              void* workspace, hipStream_t stream);
 
 /*
  * Producer-fused quantization: the step that feeds a linear, computed and
@@ -239,7 +253,7 @@ fp8_status fp8_add_rmsnorm_quant_dynamic(const uint16_t* h_bf16, int64_t ld_h,
                                          int64_t rows, int64_t cols, float eps,
                                          uint16_t* y_out_bf16, int64_t ld_y,
                                          uint8_t* q_e4m3, int64_t ld_q, float* scale_out,
-                                         void* workspace, void* stream);
+                                         void* workspace, hipStream_t stream);
 
 /*
  * m = bf16(silu(g) * u), silu(g) = g / (1 + exp(-g)) in float64, where row r
@@ -256,7 +270,7 @@ fp8_status fp8_add_rmsnorm_quant_dynamic(const uint16_t* h_bf16, int64_t ld_h,
 fp8_status fp8_silu_mul_quant_dynamic(const uint16_t* gu_bf16, int64_t ld_gu, int64_t rows,
                                       int64_t cols, uint16_t* y_out_bf16, int64_t ld_y,
                                       uint8_t* q_e4m3, int64_t ld_q, float* scale_out,
-                                      void* workspace, void* stream);
+                                      void* workspace, hipStream_t stream);
 
 /*
  * fp8 formats.  E4M3 is the pages' float8_e4m3fn (max 448) and the format of
@@ -272,19 +286,26 @@ typedef enum { FP8_FORMAT_E4M3 = 0, FP8_FORMAT_E5M2 = 1 } fp8_format;
 
 fp8_status fp8_quant_dynamic_fmt(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
                                  fp8_format fmt, uint8_t* q, int64_t ld_q, float* scale_out,
-                                 void* workspace, void* stream);
+                                 void* workspace, hipStream_t stream);
 fp8_status fp8_quant_static_fmt(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
                                 fp8_format fmt, const float* scale, uint8_t* q, int64_t ld_q,
-                                void* stream);
+                                hipStream_t stream);
 fp8_status fp8_quant_dynamic_per_row_fmt(const uint16_t* x_bf16, int64_t rows, int64_t cols,
                                          int64_t ld_x, fp8_format fmt, uint8_t* q, int64_t ld_q,
-                                         float* scales_out, void* stream);
-/* a_q holds fmt_a codes, w_q fmt_w codes (any mix); otherwise as fp8_scaled_mm. */
+                                         float* scales_out, hipStream_t stream);
+/*
+ * fp8_scaled_mm with the format of each operand and the accumulation mode
+ * as arguments: a_q holds fmt_a codes, w_q fmt_w codes (any mix), and
+ * `accum` selects how products are summed (see fp8_accum_mode;
+ * FP8_ACCUM_FP32 gives exactly fp8_scaled_mm).  Otherwise, and for its
+ * errors (plus INVALID_ARG for an unknown format or accumulation mode), as
+ * fp8_scaled_mm.
+ */
 fp8_status fp8_scaled_mm_fmt(const uint8_t* a_q, int64_t lda, fp8_format fmt_a,
                              const uint8_t* w_q, int64_t ldw, fp8_format fmt_w,
                              const float* s_a, const float* s_w, fp8_scale_mode mode,
                              fp8_accum_mode accum, const uint16_t* bias_bf16, uint16_t* out_bf16,
-                             int64_t ldo, int64_t M, int64_t N, int64_t K, void* stream);
+                             int64_t ldo, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 /* Text describing the calling thread's most recent non-OK status. */
 const char* fp8_last_error(void);

@@ -42,9 +42,52 @@ def bf16_to_f64(bits):
 def abs_dot(aq, sa, wq, sw, per_channel, fmt_a="e4m3", fmt_w="e4m3"):
     """sum_k |dec(a[m,k]) * dec(w[n,k])| * s_a * s_w[n] (fp64)."""
     da = np.abs(oracle.FORMATS[fmt_a][0](aq)); dw = np.abs(oracle.FORMATS[fmt_w][0](wq))
+    return (da @ dw.T) * float(sa) * _col_scales(sw, per_channel, wq.shape[0])[None, :]
+
+
+def _col_scales(sw, per_channel, n):
     s = np.asarray(sw, np.float32).astype(np.float64)
-    col = s if per_channel else np.full(wq.shape[0], s[0])
-    return (da @ dw.T) * float(sa) * col[None, :]
+    return s if per_channel else np.full(n, s[0])
+
+
+def group_max_dot(aq, sa, wq, sw, per_channel, fmt_a="e4m3", fmt_w="e4m3", group=8):
+    """sum over aligned k-groups g of (max_{k in g} |a_k|) (max_{k in g} |w_k|),
+    scaled: an upper bound of sum_g max_{k in g} |a_k w_k| (fp64)."""
+    k = aq.shape[1]
+    kp = -(-k // group) * group
+
+    def gmax(q, fmt):
+        d = np.abs(oracle.FORMATS[fmt][0](q))
+        d = np.pad(d, ((0, 0), (0, kp - k)))
+        return d.reshape(q.shape[0], kp // group, group).max(axis=2)
+    return (gmax(aq, fmt_a) @ gmax(wq, fmt_w).T) * float(sa) * _col_scales(sw, per_channel, wq.shape[0])[None, :]
+
+
+def fp8_accum_bound(aq, sa, wq, sw, per_channel, ref, bias_bits=None, fmt_a="e4m3", fmt_w="e4m3"):
+    """Element-wise error bound of the fp8 matrix-core accumulation mode.
+
+    From the pinned rule (tests/test_gpu_fp8_mfma_groups.py): each aligned
+    group of 8 products keeps 13 bits below its largest product, so each of
+    its 8 products loses less than 2^-13 of that product, at most
+    2^-10 * max_g |p| per group; the group sums then accumulate in fp32,
+    K/8 additions of relative error 2^-24 at most on partial sums bounded by
+    sum_k |p|; the epilogue's float32 fma and the bf16 rounding add at most
+    2^-8 of the output (and of the bias).
+    """
+    k = aq.shape[1]
+    g = group_max_dot(aq, sa, wq, sw, per_channel, fmt_a, fmt_w)
+    ad = abs_dot(aq, sa, wq, sw, per_channel, fmt_a, fmt_w)
+    bound = 2.0 ** -10 * g + (k / 8 + 2) * 2.0 ** -24 * ad + 2.0 ** -8 * np.abs(ref)
+    if bias_bits is not None:
+        bound = bound + 2.0 ** -8 * np.abs(bf16_to_f64(bias_bits))[None, :]
+    return bound
+
+
+def clause2_violations(out, ref):
+    """Elements with |ref| > 1e-3 whose relative error exceeds 2e-2."""
+    err = np.abs(out - ref)
+    big = np.abs(ref) > REL_FLOOR
+    return int(np.count_nonzero(err[big] > REL * np.abs(ref[big])))
 
 
 def assert_gemm_close(out_bits, ref, aq, sa, wq, sw, per_channel, rows=None, bias_bits=None, accum="fp32",
@@ -54,10 +97,11 @@ def assert_gemm_close(out_bits, ref, aq, sa, wq, sw, per_channel, rows=None, bia
     rows: the output rows that `ref` covers (ref has len(rows) rows).
     Both modes: |err| <= 1e-2 * ||a_m|| * ||w_n|| (+ 2^-8 |bias_n|, the bf16
     rounding of the bias part).  accum="fp32": also |err|/|ref| <= 2e-2 where
-    |ref| > 1e-3.  accum="fp8" (fp8 matrix-core sums, 13 bits below the
-    largest product of each group of 8): |err| <= 2^-8 * sum_k |a_k w_k| + bf16
-    rounding, and the RMS over elements of (err - bf16 rounding allowance) /
-    sum_k |a_k w_k| <= 2^-13.
+    |ref| > 1e-3; returns the largest such relative error.  accum="fp8"
+    (fp8 matrix-core sums, 13 bits below the largest product of each group
+    of 8): |err| <= fp8_accum_bound element-wise; returns the count of
+    elements that break the relative clause, which that mode does not meet
+    on every input.
     """
     out = bf16_to_f64(out_bits if rows is None else out_bits[rows])
     a_sub = aq if rows is None else aq[rows]
@@ -70,16 +114,11 @@ def assert_gemm_close(out_bits, ref, aq, sa, wq, sw, per_channel, rows=None, bia
     bad = err > bound
     assert not bad.any(), f"{bad.sum()} elements over the norm bound; worst err/bound {np.max(err / np.maximum(bound, 1e-300)):.3g}"
     if accum == "fp8":
-        ad = abs_dot(a_sub, sa, wq, sw, per_channel, fmt_a, fmt_w)
-        lim = 2.0 ** -8 * ad + 2.0 ** -8 * np.abs(ref)
+        lim = fp8_accum_bound(a_sub, sa, wq, sw, per_channel, ref, bias_bits, fmt_a, fmt_w)
         over = err > lim
-        assert not over.any(), f"{over.sum()} elements over the fp8-accumulation bound"
-        # accumulation error beyond the output's own bf16 rounding
-        acc_err = np.maximum(err - 2.0 ** -8 * np.abs(ref), 0.0)
-        ratio = acc_err[ad > 0] / ad[ad > 0]
-        rms = float(np.sqrt(np.mean(ratio ** 2))) if ratio.size else 0.0
-        assert rms <= 2.0 ** -13, f"RMS err/sum|a w| = {rms:.3g} > 2^-13"
-        return rms
+        assert not over.any(), (f"{over.sum()} elements over the fp8-accumulation bound; worst err/bound "
+                                f"{np.max(err / np.maximum(lim, 1e-300)):.3g}")
+        return clause2_violations(out, ref)
     big = np.abs(ref) > REL_FLOOR
     rel = err[big] / np.abs(ref[big])
     assert rel.size == 0 or rel.max() <= REL, f"max relative error {rel.max():.3g} > {REL}"

@@ -74,12 +74,13 @@ def test_quant_static_and_per_row_reject_bad_arguments(lib):
 
 
 def test_scaled_mm_rejects_bad_arguments(lib):
+    # the boundary's argument list: a_q, lda, w_q, ldw, s_a, s_w, mode, bias, out, ldo, M, N, K, stream
     f = lib.fp8_scaled_mm
-    good = dict(a=P, lda=64, w=P, ldw=64, sa=P, sw=P, mode=0, accum=0, bias=NULL, out=P, ldo=32, M=4, N=32, K=64)
+    good = dict(a=P, lda=64, w=P, ldw=64, sa=P, sw=P, mode=0, bias=NULL, out=P, ldo=32, M=4, N=32, K=64)
 
     def call(**kw):
         a = dict(good, **kw)
-        return f(a["a"], a["lda"], a["w"], a["ldw"], a["sa"], a["sw"], a["mode"], a["accum"], a["bias"], a["out"],
+        return f(a["a"], a["lda"], a["w"], a["ldw"], a["sa"], a["sw"], a["mode"], a["bias"], a["out"],
                  a["ldo"], a["M"], a["N"], a["K"], NULL)
     assert call(M=-1) == INVALID
     assert call(N=-2) == INVALID
@@ -88,12 +89,24 @@ def test_scaled_mm_rejects_bad_arguments(lib):
     assert call(ldw=10) == INVALID
     assert call(ldo=31) == INVALID
     assert call(mode=2) == INVALID and "mode" in _err(lib)
-    assert call(accum=5) == INVALID and "accumulation" in _err(lib)
     for p in ("a", "w", "sa", "sw", "out"):
         assert call(**{p: NULL}) == INVALID, p
+    assert call(M=2 ** 31) == UNSUPPORTED
+    assert call(K=2 ** 30, lda=2 ** 30, ldw=2 ** 30) == UNSUPPORTED
     # empty problems are valid no-ops that launch nothing
     assert call(M=0) == OK
     assert call(N=0, ldo=0) == OK
+
+
+def test_scaled_mm_signature_is_the_boundarys():
+    """fp8_scaled_mm takes (a_q, lda, w_q, ldw, s_a, s_w, mode, bias, out, ldo,
+    M, N, K, stream): no accumulation argument between mode and bias."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    decl = re.search(r"fp8_status\s+fp8_scaled_mm\s*\((.*?)\);", text, flags=re.S).group(1)
+    names = [re.sub(r"[^A-Za-z0-9_]", " ", a).split()[-1] for a in decl.split(",")]
+    assert names == ["a_q", "lda", "w_q", "ldw", "s_a", "s_w", "mode", "bias_bf16", "out_bf16", "ldo",
+                     "M", "N", "K", "stream"]
+    assert len(fp8.SIGNATURES["fp8_scaled_mm"][1]) == 14
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
@@ -131,6 +144,8 @@ def test_format_arguments_are_validated(lib):
     assert lib.fp8_quant_static_fmt(P, 2, 4, 4, -1, P, P, 4, NULL) == INVALID
     assert lib.fp8_quant_dynamic_per_row_fmt(P, 2, 4, 4, 7, P, 4, P, NULL) == INVALID
     f = lib.fp8_scaled_mm_fmt
+    assert f(P, 64, 0, P, 64, 0, P, P, 0, 5, NULL, P, 32, 4, 32, 64, NULL) == INVALID   # accumulation mode
+    assert "accumulation" in _err(lib)
     assert f(P, 64, 0, P, 64, 3, P, P, 0, 0, NULL, P, 32, 4, 32, 64, NULL) == INVALID
     assert f(P, 64, 5, P, 64, 1, P, P, 0, 0, NULL, P, 32, 4, 32, 64, NULL) == INVALID
     assert f(P, 63, 1, P, 64, 1, P, P, 0, 0, NULL, P, 32, 4, 32, 64, NULL) == INVALID   # lda < K

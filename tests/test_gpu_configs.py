@@ -36,7 +36,12 @@ def _linear_case(cfg, m, k, n, per_channel, outliers, rowmul, sub, rows=None, ac
     ref = oracle.scaled_mm(aq, wq, sa, sw, per_channel)
     ob = host_bf16_bits(out)
     stat = assert_gemm_close(ob if rows is None else ob[rows], ref, aq, sa, wq, sw, per_channel, accum=accum)
-    say(f"  ok ({'max rel err' if accum == 'fp32' else 'rms err/sum|aw|'} {stat:.3g})")
+    if accum == "fp32":
+        say(f"  ok (max rel err {stat:.3g})")
+    else:
+        n_big = int(np.count_nonzero(np.abs(ref) > 1e-3))
+        say(f"  ok (within the fp8-accumulation bound; relative clause broken on {stat} of {n_big} "
+            f"elements with |ref| > 1e-3)")
 
 
 def test_single_linear_per_tensor_16x4096x4096():

@@ -84,7 +84,8 @@ def test_linear_empty_problems():
     # N == 0: the codes and the scale are still produced
     xb = synth.activations(5, 4, 64)
     w0 = torch.zeros((0, 64), dtype=torch.uint8, device="cuda")
-    out, a_q, s_a = fp8.linear_dynamic(dev_bf16(xb), w0, d["s_w"], True, workspace=ws)
+    s0 = torch.zeros(0, dtype=torch.float32, device="cuda")   # one scale per (absent) output channel
+    out, a_q, s_a = fp8.linear_dynamic(dev_bf16(xb), w0, s0, True, workspace=ws)
     aq_ref, sa_ref = oracle.quant_dynamic(xb)
     torch.cuda.synchronize()
     assert out.shape == (4, 0) and host_f32(s_a)[0] == sa_ref and np.array_equal(host_u8(a_q), aq_ref)

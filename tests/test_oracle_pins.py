@@ -302,6 +302,51 @@ def test_tolerance_met_by_a_float32_blocked_accumulator():
     assert np.all(err[big] / np.abs(ref[big]) <= 2e-2)
 
 
+def test_dequant_row_norms_closed_forms():
+    """The tolerance's norms are L2 norms of the dequantized rows, each row with
+    its own scale: closed forms that an L1 norm, a squared or doubled scale,
+    a scale applied to the wrong row, or a column norm would all fail."""
+    # a row of K codes 0x38 (1.0) at scale s has norm s * sqrt(K)
+    for K, s in [(16, 3.0), (4096, 0.25), (1, 7.0)]:
+        q = np.full((1, K), 0x38, np.uint8)
+        assert oracle.dequant_row_norms(q, [np.float32(s)], per_row=False)[0] == s * np.sqrt(K)
+    # one-hot rows of +-448 (0x7E / 0xFE) have norm 448 * s, whatever K
+    q = np.zeros((2, 40), np.uint8)
+    q[0, 3], q[1, 39] = 0x7E, 0xFE
+    assert oracle.dequant_row_norms(q, [np.float32(0.5)], per_row=False).tolist() == [224.0, 224.0]
+    # 3-4-5: codes 0x44 (3.0) and 0xC8 (-4.0) give 5 * s (L1 would give 7 * s)
+    q = np.array([[0x44, 0x00, 0xC8]], np.uint8)
+    assert oracle.dequant_row_norms(q, [np.float32(3.0)], per_row=False)[0] == 15.0
+    # per-row scales land on their own rows (row r of 0x40 = 2.0 in 4 columns: norm 4 * s_r)
+    q = np.full((3, 4), 0x40, np.uint8)
+    s = np.array([0.5, 2.0, 8.0], np.float32)
+    assert oracle.dequant_row_norms(q, s, per_row=True).tolist() == [2.0, 8.0, 32.0]
+    # per tensor: the one scale for every row; rows differ only by their codes
+    q = np.array([[0x38, 0x38, 0x00, 0x00], [0x40, 0x40, 0x40, 0x40]], np.uint8)
+    assert oracle.dequant_row_norms(q, [np.float32(2.0)], per_row=False).tolist() == [2.0 * np.sqrt(2.0), 8.0]
+    # e5m2: 0x3C is 1.0 and 0x7B the largest value 57344
+    q = np.array([[0x3C, 0x3C, 0x3C, 0x3C], [0x7B, 0, 0, 0]], np.uint8)
+    assert oracle.dequant_row_norms(q, [np.float32(0.5)], per_row=False, fmt="e5m2").tolist() == [1.0, 28672.0]
+
+
+def test_dequant_row_norms_bound_is_cauchy_schwarz_tight():
+    """|sum_k a_k w_k| <= ||a|| ||w||, with equality for parallel rows: the
+    norm product is the largest output the two rows can give, so the 1e-2
+    tolerance is 1% of the largest possible magnitude of that output."""
+    rng = np.random.default_rng(3)
+    aq = oracle.encode(rng.standard_normal((5, 64)).astype(np.float32) * 50)
+    wq = oracle.encode(rng.standard_normal((7, 64)).astype(np.float32) * 50)
+    sa, sw = np.float32(0.125), rng.uniform(0.5, 2, 7).astype(np.float32)
+    out = np.abs(oracle.scaled_mm(aq, wq, sa, sw, True))
+    prod = np.outer(oracle.dequant_row_norms(aq, [sa], False), oracle.dequant_row_norms(wq, sw, True))
+    assert np.all(out <= prod * (1 + 1e-12))
+    # parallel rows attain it
+    same = aq[:1].copy()
+    out1 = abs(oracle.scaled_mm(same, same, sa, np.array([sa]), False)[0, 0])
+    n1 = oracle.dequant_row_norms(same, [sa], False)[0]
+    assert out1 == pytest.approx(n1 * n1, rel=1e-14)
+
+
 # ------------------------------------------------------------- O-P12 memory
 def test_one_byte_per_weight():
     w = synth.weights(4, 1030, 96)
@@ -318,3 +363,51 @@ def test_bf16_rounding_helper():
     x = np.random.default_rng(1).standard_normal(1000).astype(np.float32)
     assert np.array_equal(oracle.to_bf16_rne(x.astype(np.float64)),
                           oracle.bf16_bits_to_f32(synth.f32_to_bf16_bits(x)).astype(np.float64))
+
+
+# ------------------------------------- fp8 matrix-core accumulation bound
+def _emulate_group_sums(da, dw, toward_zero):
+    """The fp8 matrix cores' summation rule, emulated exactly: per aligned
+    group of 8 k positions, every product is cut to a multiple of
+    2^(E - 13), E = floor(log2(largest |product| of the group)); the group
+    sums are then added in float32 in k order."""
+    m, k = da.shape
+    n = dw.shape[0]
+    kp = -(-k // 8) * 8
+    pa = np.pad(da, ((0, 0), (0, kp - k))).reshape(m, 1, kp // 8, 8)
+    pw = np.pad(dw, ((0, 0), (0, kp - k))).reshape(1, n, kp // 8, 8)
+    p = pa * pw                                            # exact in fp64 (e4m3 products)
+    mx = np.abs(p).max(axis=3, keepdims=True)
+    e = np.floor(np.log2(np.where(mx > 0, mx, 1.0)))
+    u = np.ldexp(1.0, (e - 13).astype(np.int64))
+    cut = (np.trunc(p / u) if toward_zero else np.floor(p / u)) * u
+    gs = cut.sum(axis=3)                                   # exact: a few multiples of u
+    acc = np.zeros((m, n), np.float32)
+    for g in range(gs.shape[2]):
+        acc = (acc + gs[:, :, g].astype(np.float32)).astype(np.float32)
+    return acc
+
+
+@pytest.mark.parametrize("toward_zero", [True, False])
+def test_fp8_accum_bound_holds_for_the_group_rule(toward_zero):
+    """The element-wise bound the fp8 accumulation mode is tested against
+    holds for an exact emulation of the rule it is derived from, on the
+    prefill statistics (outlier activation columns, row-scaled weights)."""
+    import sys, os
+    sys.path.insert(0, os.path.dirname(__file__))
+    from _helpers import fp8_accum_bound, clause2_violations
+    k = 4096
+    a_bits = synth.activations(3, 48, k, outliers=True)
+    w_bits = synth.weights(3, 96, k, row_multipliers=True)
+    aq, sa = oracle.quant_dynamic(a_bits); wq, sw = oracle.quant_weight(w_bits, True)
+    ref = oracle.scaled_mm(aq, wq, sa, sw, True)
+    acc = _emulate_group_sums(oracle.decode(aq), oracle.decode(wq), toward_zero)
+    out = oracle.bf16_bits_to_f32(synth.f32_to_bf16_bits(acc * (np.float32(sa) * sw[None, :]))).astype(np.float64)
+    err = np.abs(out - ref)
+    bound = fp8_accum_bound(aq, sa, wq, sw, True, ref)
+    assert np.all(err <= bound)
+    # the emulated rule does lose precision the bf16-output rounding alone would not explain
+    assert np.any(err > 2.0 ** -8 * np.abs(ref))
+    # and the bound is not vacuous: the worst element uses a tenth of it or more
+    assert np.max(err / bound) > 0.1
+    clause2_violations(out, ref)   # counted, not bounded: the relative clause is not this mode's guarantee
