@@ -44,6 +44,8 @@ SIGNATURES = {
     "fp8_linear_workspace_bytes": (ctypes.c_size_t, []),
     "fp8_linear_dynamic": (_I, [_P, _I64, _P, _I64, _P, _I, _I, _P, _P, _I64, _P, _P, _I64, _I64, _I64, _I64,
                                 _P, _P]),
+    "fp8_linear_dynamic_noalloc": (_I, [_P, _I64, _P, _I64, _P, _I, _I, _P, _P, _I64, _P, _P, _I64, _I64, _I64,
+                                        _I64, _P]),
 }
 
 _lib = None
@@ -292,6 +294,24 @@ def linear_dynamic(x, w_q, s_w, per_channel, bias=None, workspace=None, a_q=None
                                     M, N, K, _ptr(workspace), _stream()),
            "fp8_linear_dynamic")
     return out, a_q, s_a
+
+
+def linear_dynamic_noalloc(x, w_q, s_w, per_channel, bias, a_q, s_a, out, accum="fp32"):
+    """linear_dynamic for callers that cannot allocate: every output is the
+    caller's, and the quantization's scratch is the library's own per-device
+    array (calls that overlap on one device race).  Returns out."""
+    acc = _accum(accum)
+    _mat(x, "x", torch.bfloat16)
+    dev = x.device
+    M, K = x.shape
+    _mat(a_q, "a_q", torch.uint8, (M, K), dev)
+    M, N, K, out = _gemm_operands(a_q, w_q, s_a, s_w, per_channel, bias, out)
+    mode = FP8_SCALE_PER_CHANNEL if per_channel else FP8_SCALE_PER_TENSOR
+    _check(lib().fp8_linear_dynamic_noalloc(_ptr(x), x.stride(0), _ptr(w_q), w_q.stride(0), _ptr(s_w), mode, acc,
+                                            _ptr(bias), _ptr(a_q), a_q.stride(0), _ptr(s_a), _ptr(out),
+                                            out.stride(0), M, N, K, _stream()),
+           "fp8_linear_dynamic_noalloc")
+    return out
 
 
 def linear(x, w_q, s_w, per_channel, bias=None, workspace=None, accum="fp32", fmt_a="e4m3", fmt_w="e4m3"):

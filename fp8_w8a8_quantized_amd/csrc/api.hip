@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <stdarg.h>
 
+#include <mutex>
+
 #include "../../include/fp8w8a8.h"
 #include "internal.h"
 
@@ -45,6 +47,79 @@ fp8_status check_quant(const char* fn, const uint16_t* x, int64_t rows, int64_t 
 fp8_status check_fmt(const char* fn, fp8_format f) {
   if (f != FP8_FORMAT_E4M3 && f != FP8_FORMAT_E5M2) return fail(FP8_ERR_INVALID_ARG, "%s: unknown format %d", fn, (int)f);
   return FP8_OK;
+}
+
+// ---- scratch of the no-allocation entry point ----------------------------
+// The dynamic quantization's per-block maxima (quant_workspace_bytes(), the
+// same for every size) live in this array instead of a caller workspace.
+// Each device the library runs on holds its own copy until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory: its
+// device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and only that address is handed to kernels.
+constexpr size_t kScratchBytes = 4096;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address, looked up on the first call made
+// on that device.
+fp8_status scratch_for_current_device(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FP8_ERR_HIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FP8_ERR_UNSUPPORTED, "%s: device index %d out of range", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(FP8_ERR_HIP, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s", fn, dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FP8_OK;
+}
+
+// The whole linear: host validation, then the dynamic quantization and the
+// scaled GEMM on its codes.  use_scratch: the quantization's per-block
+// maxima go to this device's scratch array instead of `workspace`.
+fp8_status linear_impl(const char* fn, const uint16_t* x_bf16, int64_t ld_x, const uint8_t* w_q, int64_t ldw,
+                       const float* s_w, fp8_scale_mode mode, fp8_accum_mode accum, const uint16_t* bias_bf16,
+                       uint8_t* a_q, int64_t ld_aq, float* s_a_out, uint16_t* out_bf16, int64_t ldo, int64_t M,
+                       int64_t N, int64_t K, void* workspace, bool use_scratch, hipStream_t stream) {
+  if (M < 0 || N < 0) return fail(FP8_ERR_INVALID_ARG, "%s: negative M or N (M=%lld, N=%lld)", fn,
+                                  (long long)M, (long long)N);
+  if (K < 1) return fail(FP8_ERR_INVALID_ARG, "%s: K must be >= 1 (K=%lld)", fn, (long long)K);
+  if (ld_x < K || ld_aq < K || ldw < K) return fail(FP8_ERR_INVALID_ARG, "%s: ld_x/ld_aq/ldw smaller than K", fn);
+  if (ldo < N) return fail(FP8_ERR_INVALID_ARG, "%s: ldo smaller than N", fn);
+  if (mode != FP8_SCALE_PER_TENSOR && mode != FP8_SCALE_PER_CHANNEL)
+    return fail(FP8_ERR_INVALID_ARG, "%s: unknown scale mode %d", fn, (int)mode);
+  if (accum != FP8_ACCUM_FP32 && accum != FP8_ACCUM_FP8_MFMA)
+    return fail(FP8_ERR_INVALID_ARG, "%s: unknown accumulation mode %d", fn, (int)accum);
+  // pointers the problem touches: x and a_q when M > 0, the GEMM's when M and N are
+  if (s_a_out == nullptr || (M > 0 && (x_bf16 == nullptr || a_q == nullptr || (!use_scratch && workspace == nullptr))) ||
+      (M > 0 && N > 0 && (w_q == nullptr || s_w == nullptr || out_bf16 == nullptr)))
+    return fail(FP8_ERR_INVALID_ARG, "%s: null required pointer", fn);
+  if (M >= (1ll << 31) || N >= (1ll << 31) || K >= (1ll << 30) || ldw >= (1ll << 40) || ld_aq >= (1ll << 40) ||
+      M * ((K + 7) / 8) >= (1ll << 31))
+    return fail(FP8_ERR_UNSUPPORTED, "%s: problem too large", fn);
+  if (use_scratch) {
+    if (fp8w8a8::quant_workspace_bytes() > kScratchBytes)
+      return fail(FP8_ERR_UNSUPPORTED, "%s: the quantization needs %zu bytes of scratch, the library holds %zu", fn,
+                  fp8w8a8::quant_workspace_bytes(), kScratchBytes);
+    fp8_status st = scratch_for_current_device(fn, &workspace);
+    if (st != FP8_OK) return st;
+  }
+  // the quantization, then the GEMM on its codes (nothing to multiply for M == 0 or N == 0)
+  fp8_status st = hip_status(fp8w8a8::launch_quant_dynamic(x_bf16, M, K, ld_x, FP8_FORMAT_E4M3, a_q, ld_aq,
+                                                           s_a_out, workspace, stream),
+                             fn);
+  if (st != FP8_OK || M == 0 || N == 0) return st;
+  return fp8_scaled_mm_fmt(a_q, ld_aq, FP8_FORMAT_E4M3, w_q, ldw, FP8_FORMAT_E4M3, s_a_out, s_w, mode, accum,
+                           bias_bf16, out_bf16, ldo, M, N, K, stream);
 }
 
 }  // namespace
@@ -206,30 +281,17 @@ fp8_status fp8_linear_dynamic(const uint16_t* x_bf16, int64_t ld_x, const uint8_
                               const uint16_t* bias_bf16, uint8_t* a_q, int64_t ld_aq, float* s_a_out,
                               uint16_t* out_bf16, int64_t ldo, int64_t M, int64_t N, int64_t K, void* workspace,
                               hipStream_t stream) {
-  const char* fn = "fp8_linear_dynamic";
-  if (M < 0 || N < 0) return fail(FP8_ERR_INVALID_ARG, "%s: negative M or N (M=%lld, N=%lld)", fn,
-                                  (long long)M, (long long)N);
-  if (K < 1) return fail(FP8_ERR_INVALID_ARG, "%s: K must be >= 1 (K=%lld)", fn, (long long)K);
-  if (ld_x < K || ld_aq < K || ldw < K) return fail(FP8_ERR_INVALID_ARG, "%s: ld_x/ld_aq/ldw smaller than K", fn);
-  if (ldo < N) return fail(FP8_ERR_INVALID_ARG, "%s: ldo smaller than N", fn);
-  if (mode != FP8_SCALE_PER_TENSOR && mode != FP8_SCALE_PER_CHANNEL)
-    return fail(FP8_ERR_INVALID_ARG, "%s: unknown scale mode %d", fn, (int)mode);
-  if (accum != FP8_ACCUM_FP32 && accum != FP8_ACCUM_FP8_MFMA)
-    return fail(FP8_ERR_INVALID_ARG, "%s: unknown accumulation mode %d", fn, (int)accum);
-  // pointers the problem touches: x and a_q when M > 0, the GEMM's when M and N are
-  if (s_a_out == nullptr || (M > 0 && (x_bf16 == nullptr || a_q == nullptr || workspace == nullptr)) ||
-      (M > 0 && N > 0 && (w_q == nullptr || s_w == nullptr || out_bf16 == nullptr)))
-    return fail(FP8_ERR_INVALID_ARG, "%s: null required pointer", fn);
-  if (M >= (1ll << 31) || N >= (1ll << 31) || K >= (1ll << 30) || ldw >= (1ll << 40) || ld_aq >= (1ll << 40) ||
-      M * ((K + 7) / 8) >= (1ll << 31))
-    return fail(FP8_ERR_UNSUPPORTED, "%s: problem too large", fn);
-  // the quantization, then the GEMM on its codes (nothing to multiply for M == 0 or N == 0)
-  fp8_status st = hip_status(fp8w8a8::launch_quant_dynamic(x_bf16, M, K, ld_x, FP8_FORMAT_E4M3, a_q, ld_aq,
-                                                           s_a_out, workspace, stream),
-                             fn);
-  if (st != FP8_OK || M == 0 || N == 0) return st;
-  return fp8_scaled_mm_fmt(a_q, ld_aq, FP8_FORMAT_E4M3, w_q, ldw, FP8_FORMAT_E4M3, s_a_out, s_w, mode, accum,
-                           bias_bf16, out_bf16, ldo, M, N, K, stream);
+  return linear_impl("fp8_linear_dynamic", x_bf16, ld_x, w_q, ldw, s_w, mode, accum, bias_bf16, a_q, ld_aq, s_a_out,
+                     out_bf16, ldo, M, N, K, workspace, false, stream);
+}
+
+fp8_status fp8_linear_dynamic_noalloc(const uint16_t* x_bf16, int64_t ld_x, const uint8_t* w_q, int64_t ldw,
+                                      const float* s_w, fp8_scale_mode mode, fp8_accum_mode accum,
+                                      const uint16_t* bias_bf16, uint8_t* a_q, int64_t ld_aq, float* s_a_out,
+                                      uint16_t* out_bf16, int64_t ldo, int64_t M, int64_t N, int64_t K,
+                                      hipStream_t stream) {
+  return linear_impl("fp8_linear_dynamic_noalloc", x_bf16, ld_x, w_q, ldw, s_w, mode, accum, bias_bf16, a_q, ld_aq,
+                     s_a_out, out_bf16, ldo, M, N, K, nullptr, true, stream);
 }
 
 fp8_status fp8_scaled_mm(const uint8_t* a_q, int64_t lda, const uint8_t* w_q, int64_t ldw, const float* s_a,

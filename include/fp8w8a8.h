@@ -214,6 +214,26 @@ fp8_status fp8_linear_dynamic(const uint16_t* x_bf16, int64_t ld_x, const uint8_
                               void* workspace, hipStream_t stream);
 
 /*
+ * fp8_linear_dynamic for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops and harnesses that forbid
+ * allocation.  The arguments and results are fp8_linear_dynamic's without
+ * the workspace: the quantization's scratch (4 KiB of per-block maxima,
+ * the same for every problem size) is a fixed array inside the library,
+ * one per device, held until the process ends.  The call allocates
+ * nothing; its first call on a device looks up that device's array.
+ * Every call on a device shares that array, so calls that overlap on one
+ * device (concurrent streams, or threads) race and must be serialized by
+ * the caller; nothing in it needs to start at zero.
+ * Errors: as fp8_linear_dynamic (no workspace argument to check);
+ * FP8_ERR_HIP if the array's address cannot be looked up.
+ */
+fp8_status fp8_linear_dynamic_noalloc(const uint16_t* x_bf16, int64_t ld_x, const uint8_t* w_q, int64_t ldw,
+                                      const float* s_w, fp8_scale_mode mode, fp8_accum_mode accum,
+                                      const uint16_t* bias_bf16, uint8_t* a_q, int64_t ld_aq, float* s_a_out,
+                                      uint16_t* out_bf16, int64_t ldo, int64_t M, int64_t N, int64_t K,
+                                      hipStream_t stream);
+
+/*
  * Producer-fused quantization: the step that feeds a linear, computed and
  * quantized in the same pass, so its bf16 result never travels through
  * memory.  The review of "[WIP] FP8 support" (text-generation-inference PR

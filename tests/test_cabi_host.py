@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
         "fp8_quant_dynamic_per_row", "fp8_scaled_mm", "fp8_last_error",
         "fp8_norm_quant_workspace_bytes", "fp8_add_rmsnorm_quant_dynamic", "fp8_silu_mul_quant_dynamic",
         "fp8_quant_dynamic_fmt", "fp8_quant_static_fmt", "fp8_quant_dynamic_per_row_fmt", "fp8_scaled_mm_fmt",
-        "fp8_linear_workspace_bytes", "fp8_linear_dynamic"])
+        "fp8_linear_workspace_bytes", "fp8_linear_dynamic", "fp8_linear_dynamic_noalloc"])
 
 
 def test_library_exports_every_declared_function(lib):
@@ -173,3 +173,22 @@ def test_linear_dynamic_rejects_bad_arguments(lib):
     assert call(N=0, ldo=0, sa=NULL) == INVALID    # the scale is an output even with N == 0
     assert call(M=2 ** 31) == UNSUPPORTED
     assert lib.fp8_linear_workspace_bytes() == lib.fp8_quant_workspace_bytes()
+
+
+def test_linear_noalloc_rejects_bad_arguments(lib):
+    """Validation runs before the scratch lookup or any launch (no GPU here)."""
+    f = lib.fp8_linear_dynamic_noalloc
+    good = dict(x=P, ldx=64, w=P, ldw=64, sw=P, mode=1, accum=0, bias=NULL, aq=P, ldaq=64, sa=P, out=P, ldo=32,
+                M=4, N=32, K=64)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return f(a["x"], a["ldx"], a["w"], a["ldw"], a["sw"], a["mode"], a["accum"], a["bias"], a["aq"], a["ldaq"],
+                 a["sa"], a["out"], a["ldo"], a["M"], a["N"], a["K"], NULL)
+    assert call(M=-1) == INVALID and "fp8_linear_dynamic_noalloc" in _err(lib)
+    assert call(K=0) == INVALID
+    assert call(ldaq=63) == INVALID
+    assert call(accum=2) == INVALID
+    for p in ("x", "w", "sw", "aq", "sa", "out"):
+        assert call(**{p: NULL}) == INVALID, p
+    assert call(M=2 ** 31) == UNSUPPORTED
