@@ -9,54 +9,65 @@
 //
 // Design for CDNA4:
 //   * 256 x 256 output tile, 128 k per step; 4 waves, each owning a
-//     128 x 128 quarter as 4 x 4 blocks of v_mfma_f32_32x32x64_f8f6f4
+//     128 x 128 quarter as 4 x 4 blocks of 32 x 32 matrix-core products
 //     (256 fp32 accumulators per lane).
 //   * Both operands are K-contiguous ([M, K] and [N, K]), the matrix cores'
 //     native operand layout: every lane reads 32 contiguous k-bytes of one
 //     row, so no transposition is needed anywhere.
 //   * Persistent: one workgroup per compute unit walks tiles b, b + grid, ...
-//     The operand pipeline runs across tile boundaries (the last k step of a
-//     tile loads the next tile's first step), and the epilogue's stores
-//     drain while the next tile's first step computes.
+//     and the operand pipeline runs across tile boundaries.
 //   * Global -> LDS directly (buffer_load ... lds, no staging registers),
-//     double-buffered (2 x 64 KiB).  Out-of-range lanes (rows past M or N,
-//     k past K) return zeros through the buffer range check, so edge tiles
-//     need no branches and k tails add nothing.
-//   * In fp8 mode each step also touches, two steps ahead, this
-//     workgroup's share of the lines its XCD's concurrent tiles will read
-//     (4-byte DMA loads into a junk LDS area), so the step's own loads find
-//     them in L2 (measured: +5%; the bf16 mode, twice as long per step, does
-//     not gain from it).
-//   * Issue order within a k step (pinned with scheduling barriers): the
-//     first half's fragments, then the first half's 16 products with one
-//     block of the next step's loads and two of the second half's fragment
-//     reads after each pair, then the second half's products.  Issued in one
-//     burst, the 16 load instructions of a wave stall its instruction stream
-//     on the texture unit while the matrix pipe idles (measured: ~30% of
-//     the step even with every load hitting L2).
+//     two stages of 64 KiB.  Out-of-range lanes (rows past M or N, k past
+//     K) return zeros through the buffer range check, so edge tiles need no
+//     branches and k tails add nothing.
+//   * One barrier per k step, in its middle.  A step's products are split
+//     in two halves of 64 k.  Before the barrier the wave multiplies the
+//     first half (whose fragments it read during the previous step) and
+//     reads the second half's fragments; after it, it multiplies the second
+//     half while it reads the NEXT step's first-half fragments from the
+//     other stage and issues the DMA loads of the step after next into the
+//     stage it has just finished reading.  So no product ever waits for an
+//     LDS read at a step boundary, and the barrier, reached with products
+//     still queued in the matrix pipe, costs no idle matrix cycles when the
+//     waves arrive together.  The barrier also orders the two stage uses:
+//     every wave's second-half reads of this stage and every wave's loads
+//     of the other stage are complete at it.
+//   * In fp8 mode each step also touches, one step ahead of its DMA loads,
+//     this workgroup's share of the lines its XCD's concurrent tiles will
+//     read (4-byte DMA loads into a junk LDS area), so the DMA loads find
+//     them in L2.
+//   * Loads and fragment reads are spread between pairs of products (pinned
+//     with scheduling barriers): issued in one burst, a wave's load
+//     instructions stall its instruction stream on the texture unit while
+//     the matrix pipe idles.
 //   * LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at
 //     position c ^ (r & 7) ^ ((r >> 3) & 1), so the rows that consecutive
 //     lanes read land in different bank groups.
-//   * Epilogue through LDS: each wave parks 32 accumulator rows at a time
-//     (fp32) in the stage buffer the tile's last step used, reads them back
-//     as 8 consecutive columns per lane, applies s_a * s_w[n] and the bias,
-//     and writes 16-byte bf16 chunks, a wave instruction covering four
-//     256-byte row segments.  The stores go through a buffer resource, whose
-//     range check drops rows past M.
+//   * Epilogue through LDS: a tile's last step issues no loads, so the stage
+//     it read is free; each wave parks 32 accumulator rows at a time (fp32,
+//     straight from the accumulator registers) in the part of that stage its
+//     own loads fill, reads them back as 8 consecutive columns per lane,
+//     applies s_a * s_w[n] and the bias (staged in LDS by DMA at the tile's
+//     first step, double-buffered across tiles), and writes 16-byte bf16
+//     chunks; a buffer resource's range check drops rows past M.  Then it
+//     issues the deferred loads into that same part (no other wave touches
+//     it, so no barrier is needed) and reads the next step's fragments.
 //   * Tile order: the hardware deals workgroups round-robin to the 8 XCDs;
 //     the tile index is remapped so each XCD owns a contiguous run of tiles,
 //     and that run walks groups of 8 tile-rows, so the A and W panels a
 //     group touches stay in that XCD's L2.
-//   * The accumulation is per-tile, in a fixed order: results are
+//   * The accumulation is per tile, in a fixed order: results are
 //     deterministic.
 //   * Two accumulation modes (template EXACT).  The fp8 instruction
-//     (v_mfma_f32_32x32x64_f8f6f4) sums each group of 8 products keeping
-//     only 13 bits below the group's largest product (measured on gfx950):
-//     twice the throughput, but small products beside large ones are
-//     truncated.  EXACT converts each fp8 fragment to bf16 in registers
+//     (v_mfma_f32_32x32x64_f8f6f4) sums each aligned group of 8 products
+//     keeping only 13 bits below the group's largest product (measured on
+//     gfx950): twice the throughput, but small products beside large ones
+//     are truncated.  EXACT converts each fp8 fragment to bf16 in registers
 //     (exact: every e4m3 value is a bf16 value) and runs
 //     v_mfma_f32_32x32x16_bf16, whose sums keep fp32-class precision; the
 //     LDS tiles, the loads and the HBM traffic are the same in both modes.
+
+#include <type_traits>
 
 #include "device_common.h"
 #include "internal.h"
@@ -72,23 +83,21 @@ constexpr int kThreads = 256;
 constexpr int kOperandBytes = BM * BK;  // 32 KiB per operand per stage
 constexpr int kStageBytes = 2 * kOperandBytes;
 constexpr int kGroupM = 8;
+// per-tile epilogue parameters: 256 column scales (fp32) and biases (bf16)
 constexpr int kEpiParamBytes = BN * 4 + BN * 2;
 // L2 prefetch: two 4-byte-per-lane DMA loads per wave and step, landing in a
 // junk LDS area nobody reads (512 bytes per wave)
 constexpr int kPrefetchBytes = 4 * 512;
+constexpr int kLdsBytes = 2 * kStageBytes + 2 * kEpiParamBytes + kPrefetchBytes;
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+// vector-memory instructions a wave issues besides the operand loads: the L2
+// prefetch after each step's loads (fp8 mode) and the two parameter loads at
+// a tile's first step
 constexpr int kPrefetchOps = 2;
-constexpr int kPrefetchDist = 2;
-// Epilogue: 32 rows per round, 4 rounds, 8 store instructions per round.
-constexpr int kEpiStores = 32;
-// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in
-// bits 15:14, expcnt in 6:4, lgkmcnt in 11:8; fields at their maximum do not
-// wait).  vmcnt(32) lets the previous tile's 32 epilogue stores, issued after
-// the loads being waited for, stay in flight.
-// In fp8 mode every step ends with kPrefetchOps prefetch loads, so a step's
-// wait leaves them (and after a tile, the epilogue stores issued later) in
-// flight.
-constexpr int wait_step(bool prefetching) { return wait_vmcnt(prefetching ? kPrefetchOps : 0); }
-constexpr int wait_epi(bool prefetching) { return wait_vmcnt(kEpiStores + (prefetching ? kPrefetchOps : 0)); }
+// how many steps the L2 prefetch runs ahead of the DMA loads
+constexpr int kPrefetchAhead = 1;
+constexpr int kParamOps = 2;
+constexpr int kStepLoads = 16;  // DMA instructions per wave and step (8 blocks x 2 operands)
 
 // XOR swizzle of the 16-byte chunks of a 128-byte LDS row.  The 16 rows a
 // half-wave reads at one logical chunk land on 16 distinct (bank-pair,
@@ -159,16 +168,17 @@ __device__ __forceinline__ Tile tile_at(const GemmArgs& g, int b, int tiles_m, i
 // writes whole 16-byte chunks (a fixed count of stores per tile).
 template <bool EXACT, bool VEC, int FA, int FW>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStageBytes + kEpiParamBytes + kPrefetchBytes];
-  // the tile's 256 column scales (fp32) and biases (bf16), loaded by DMA
-  float* Psc = reinterpret_cast<float*>(smem + 2 * kStageBytes);
-  uint16_t* Pbias = reinterpret_cast<uint16_t*>(smem + 2 * kStageBytes + BN * 4);
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
+  uint8_t* const params = smem + 2 * kStageBytes;  // two parameter buffers, by tile parity
+  uint8_t* const pf_junk = params + 2 * kEpiParamBytes;
 
   const int T = tiles_m * tiles_n;
+  const int KT = (g.K + BK - 1) / BK;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  constexpr int kPf = EXACT ? 0 : kPrefetchOps;
 
   // ---- loader: buffer_load_dwordx4 ... lds.  Each wave instruction fills
   // one dense 1 KiB LDS block (8 rows x 128 bytes, lane i -> bytes 16i ..
@@ -188,51 +198,69 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
   // the chunk (hence k offset) a lane fetches depends only on its row within
   // the block and on the block's parity
   const int dchunk_k0 = (dphys ^ drow_in_blk) * 16, dchunk_k1 = (dphys ^ drow_in_blk ^ 1) * 16;
-  // one block of each operand (2 instructions); dma() issues all 8 blocks
-  auto dma_part = [&](int stage, const Tile& t, int k0, bool step_valid, int i) {
-    const bool kin = step_valid && k0 + ((i & 1) ? dchunk_k1 : dchunk_k0) < g.K;
+
+  // The load cursor: the tile and k step the next DMA loads fetch.  It runs
+  // two steps ahead of the products, across tile boundaries; past the last
+  // tile its loads fetch zeros.
+  int lb = blockIdx.x, lkt = 0;
+  Tile lt = tile_at(g, lb, tiles_m, tiles_n);
+  auto advance_load = [&]() {
+    if (++lkt == KT) {
+      lkt = 0;
+      lb += gridDim.x;
+      if (lb < T) lt = tile_at(g, lb, tiles_m, tiles_n);
+    }
+  };
+  // one block of each operand of the load cursor's step (2 instructions)
+  auto dma_part = [&](int stage, int i) {
+    const int k0 = lkt * BK;
+    const bool kin = lb < T && k0 + ((i & 1) ? dchunk_k1 : dchunk_k0) < g.K;
     uint8_t* As = smem + stage * kStageBytes;
     uint8_t* Ws = As + kOperandBytes;
     const int blk = __builtin_amdgcn_readfirstlane(wave * 8 + i);
     const uint32_t oa = kin ? dvoff_a[i] + k0 : kOutOfRange;
     const uint32_t ow = kin ? dvoff_w[i] + k0 : kOutOfRange;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(t.ra, (__attribute__((address_space(3))) void*)(As + blk * 1024), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(lt.ra, (__attribute__((address_space(3))) void*)(As + blk * 1024), 16,
                                              (int)oa, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(t.rw, (__attribute__((address_space(3))) void*)(Ws + blk * 1024), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(lt.rw, (__attribute__((address_space(3))) void*)(Ws + blk * 1024), 16,
                                              (int)ow, 0, 0, 0);
   };
-  auto dma = [&](int stage, const Tile& t, int k0, bool step_valid) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dma_part(stage, t, k0, step_valid, i);
+  // The prefetch cursor: kPrefetchAhead steps ahead of the load cursor.
+  int pb = blockIdx.x, pkt = 0;
+  Tile pt = lt;
+  auto advance_prefetch = [&]() {
+    if (++pkt == KT) {
+      pkt = 0;
+      pb += gridDim.x;
+      if (pb < T) pt = tile_at(g, pb, tiles_m, tiles_n);
+    }
+  };
+  // L2 prefetch of the prefetch cursor's step, which then advances.
+  // The 32 workgroups an XCD runs at once hold 8 tile-rows x 4 tile-columns
+  // (see tile_at), so they share 8 A panels (4 tiles each) and 4 W panels
+  // (8 tiles each): this one touches rows 64 (tn % 4) .. + 63 of its A panel
+  // and 32 (tm % 8) .. + 31 of its W panel, one line per row, so together
+  // they bring each panel's step into the XCD's L2.  The loads land in a
+  // junk LDS area (no registers to hold, nothing waits on them); for other
+  // tile layouts they merely touch lines of this tile's own panels.
+  auto prefetch = [&]() {
+    const int tm = pt.m0 / BM, tn = pt.n0 / BN;
+    const bool valid = pb < T;
+    const int s = pkt * BK;
+    const uint32_t oa =
+        (valid && lane < 16) ? (uint32_t)((64 * (tn & 3) + 16 * wave + lane) * g.lda + s) : kOutOfRange;
+    const uint32_t ow =
+        (valid && lane < 8) ? (uint32_t)((32 * (tm & 7) + 8 * wave + lane) * g.ldw + s) : kOutOfRange;
+    uint8_t* J = pf_junk + __builtin_amdgcn_readfirstlane(wave * 512);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(pt.ra, (__attribute__((address_space(3))) void*)J, 4, (int)oa, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(pt.rw, (__attribute__((address_space(3))) void*)(J + 256), 4, (int)ow, 0,
+                                             0, 0);
+    advance_prefetch();
   };
 
-  const int KT = (g.K + BK - 1) / BK;
-  // L2 prefetch of step s of tile t, kPrefetchDist steps ahead of the step it
-  // feeds.  The 32 workgroups an XCD runs at once hold 8 tile-rows x 4
-  // tile-columns (see tile_at), so they share 8 A panels (4 tiles each) and
-  // 4 W panels (8 tiles each): this one touches rows 64 (tn % 4) .. + 63 of
-  // its A panel and 32 (tm % 8) .. + 31 of its W panel, one line per row,
-  // so together they bring each panel's next-but-one step into the XCD's
-  // L2 while the current step computes.  The loads land in a junk LDS area
-  // (no registers to hold, nothing waits on them); for other tile layouts
-  // they merely touch lines of this tile's own panels.
-  uint8_t* const pf_junk = smem + 2 * kStageBytes + kEpiParamBytes;
-  auto prefetch = [&](const Tile& t, int s, bool valid) {
-    const int tm = t.m0 / BM, tn = t.n0 / BN;
-    const uint32_t oa =
-        (valid && lane < 16) ? (uint32_t)((64 * (tn & 3) + 16 * wave + lane) * g.lda + s * BK) : kOutOfRange;
-    const uint32_t ow =
-        (valid && lane < 8) ? (uint32_t)((32 * (tm & 7) + 8 * wave + lane) * g.ldw + s * BK) : kOutOfRange;
-    uint8_t* J = pf_junk + __builtin_amdgcn_readfirstlane(wave * 512);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(t.ra, (__attribute__((address_space(3))) void*)J, 4, (int)oa, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(t.rw, (__attribute__((address_space(3))) void*)(J + 256), 4, (int)ow, 0,
-                                             0, 0);
-  };
   const int frow = lane & 31;          // operand row within a 32-row block
   const int fchunk = (lane >> 5) * 2;  // first of the lane's two chunks
   const float sa = *g.s_a;
-  // epilogue lane roles: 8 consecutive columns (chunk ec) of rows er + 4s
-  const int ec = lane & 15, er = lane >> 4;
 
   // scales and bias through buffer resources: a missing bias is a resource of
   // size 0, whose loads return zeros
@@ -241,166 +269,248 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
   const __amdgpu_buffer_rsrc_t rbias = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(g.bias ? g.bias : reinterpret_cast<const uint16_t*>(g.s_w)), (short)0, g.bias ? g.N * 2 : 0,
       kRsrcWord3);
+  // a tile's epilogue parameters, straight into LDS (no registers, so no wait
+  // on them lands before the epilogue), exactly kParamOps instructions per
+  // wave: wave w fetches the scales of columns 64w .. 64w + 63 and the
+  // biases of columns 64w .. 64w + 63 (two per lane for waves 0 and 1, a
+  // load of nothing for waves 2 and 3); columns past N read zeros and are
+  // never stored.
+  auto load_params = [&](const Tile& t, uint8_t* P) {
+    float* Psc = reinterpret_cast<float*>(P);
+    uint16_t* Pbias = reinterpret_cast<uint16_t*>(P + BN * 4);
+    const int nc = t.n0 + wave * 64 + lane;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsw, (__attribute__((address_space(3))) void*)(Psc + __builtin_amdgcn_readfirstlane(wave * 64)), 4,
+        (int)(g.per_channel ? (nc < g.N ? (uint32_t)nc * 4 : kOutOfRange) : 0u), 0, 0, 0);
+    // VEC: N % 8 == 0, so no dword of two biases straddles the end
+    const int nb2 = t.n0 + (wave & 1) * 128 + 2 * lane;
+    const bool bias_ok = VEC && wave < 2 && nb2 < g.N;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rbias,
+        (__attribute__((address_space(3))) void*)(wave < 2 ? Pbias + __builtin_amdgcn_readfirstlane(wave * 128)
+                                                             : reinterpret_cast<uint16_t*>(pf_junk)),
+        4, (int)(bias_ok ? (uint32_t)nb2 * 2 : kOutOfRange), 0, 0, 0);
+  };
 
-  int b = blockIdx.x;
-  Tile cur = tile_at(g, b, tiles_m, tiles_n);
-  dma(0, cur, 0, true);
-  if constexpr (!EXACT) prefetch(cur, 1, KT > 1);
-  int step = 0;  // steps issued so far over all tiles: stage parity
-  bool first = true;
-  for (; b < T; b += gridDim.x) {
-    const bool has_next = b + (int)gridDim.x < T;
-    const Tile nxt = has_next ? tile_at(g, b + gridDim.x, tiles_m, tiles_n) : cur;
+  // ---- prologue: the first two steps' loads, then the first step's
+  // first-half fragments
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dma_part(0, i);
+  advance_load();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dma_part(1, i);
+  advance_load();
+  advance_prefetch();
+  advance_prefetch();
+  if constexpr (!EXACT) {
+#pragma unroll
+    for (int d = 0; d < kPrefetchAhead; ++d) prefetch();
+  }
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt(kStepLoads + kPf * kPrefetchAhead));
+  __builtin_amdgcn_s_barrier();
+  v8i wf0[4], af0[4], wf1[4], af1[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wf0[i] = read_frag(smem + kOperandBytes, wn * 128 + i * 32 + frow, fchunk);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) af0[j] = read_frag(smem, wm * 128 + j * 32 + frow, fchunk);
 
-    const int ecol = wn * 128 + ec * 8;  // this lane's 8 output columns, within the tile
-    const bool col_ok = ecol + 8 <= cur.cols;
+  int step = 0;   // steps done over all tiles: stage parity
+  int tcount = 0;  // tiles done: parameter-buffer parity
+  v16f acc[4][4];
+  // One k step (see the design notes above).  FIRST: the tile's first step
+  // (its parameter loads).  LAST: the tile's last step, whose second half
+  // issues no loads and reads no fragments: its stage becomes the
+  // epilogue's staging area, and the loads of the step after next and the
+  // next step's fragment reads follow the epilogue.
+  auto do_step = [&](auto first_c, auto last_c, const Tile& cur, uint8_t* P) {
+    constexpr bool FIRST = decltype(first_c)::value;
+    constexpr bool LAST = decltype(last_c)::value;
+    const uint8_t* As = smem + (step & 1) * kStageBytes;
+    const uint8_t* Ws = As + kOperandBytes;
+    const uint8_t* An = smem + ((step + 1) & 1) * kStageBytes;
+    const uint8_t* Wn = An + kOperandBytes;
+    // this step's first-half fragments (read during the previous step) are in
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    if constexpr (FIRST) load_params(cur, P);
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- first half: its products, with the second half's fragment reads
+    if constexpr (!EXACT) {
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int i = (2 * p + q) >> 2, j = (2 * p + q) & 3;
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf0[i], af0[j], acc[i][j], FW, FA, 0, 0, 0,
+                                                                       0);
+        }
+        if (p < 4) wf1[p] = read_frag(Ws, wn * 128 + p * 32 + frow, 4 + fchunk);
+        else af1[p - 4] = read_frag(As, wm * 128 + (p - 4) * 32 + frow, 4 + fchunk);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        bf16x8 wb[4], ab[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wb[i] = slice_bf16<FW>(wf0[i], t);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ab[j] = slice_bf16<FA>(af0[j], t);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb[i], ab[j], acc[i][j], 0, 0, 0);
+        wf1[t] = read_frag(Ws, wn * 128 + t * 32 + frow, 4 + fchunk);
+        af1[t] = read_frag(As, wm * 128 + t * 32 + frow, 4 + fchunk);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // ---- the step's barrier.  Outstanding vector-memory operations of this
+    // wave, oldest first: the next step's loads (issued during the previous
+    // step, or after the previous tile's epilogue), their L2 prefetch, and
+    // at a tile's first step its parameter loads; in-order completion lets
+    // the wait leave everything after the loads in flight.  The second-half
+    // reads of this stage are done too, so after the barrier every wave may
+    // overwrite it.
+    if constexpr (!FIRST)
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(kPf) & kWaitLgkm0);
+    else
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(kPf + kParamOps) & kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- second half: its products, with the loads of the step after next
+    // into this stage and (but in a tile's last step) the next step's
+    // first-half fragment reads
+    if constexpr (!EXACT) {
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int i = (2 * p + q) >> 2, j = (2 * p + q) & 3;
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf1[i], af1[j], acc[i][j], FW, FA, 0, 0, 0,
+                                                                       0);
+        }
+        if constexpr (!LAST) {
+          dma_part(step & 1, p);
+          if (p == 7) {
+            advance_load();
+            prefetch();
+          }
+          if (p < 4) wf0[p] = read_frag(Wn, wn * 128 + p * 32 + frow, fchunk);
+          else af0[p - 4] = read_frag(An, wm * 128 + (p - 4) * 32 + frow, fchunk);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        bf16x8 wb[4], ab[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wb[i] = slice_bf16<FW>(wf1[i], t);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ab[j] = slice_bf16<FA>(af1[j], t);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb[i], ab[j], acc[i][j], 0, 0, 0);
+        if constexpr (!LAST) {
+          dma_part(step & 1, 2 * t);
+          dma_part(step & 1, 2 * t + 1);
+          if (t == 3) advance_load();
+          wf0[t] = read_frag(Wn, wn * 128 + t * 32 + frow, fchunk);
+          af0[t] = read_frag(An, wm * 128 + t * 32 + frow, fchunk);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    ++step;
+  };
+  using True = std::integral_constant<bool, true>;
+  using False = std::integral_constant<bool, false>;
 
-    v16f acc[4][4];
+  for (int b = blockIdx.x; b < T; b += gridDim.x, ++tcount) {
+    const Tile cur = tile_at(g, b, tiles_m, tiles_n);
+    uint8_t* const P = params + (tcount & 1) * kEpiParamBytes;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-    int kt = 0;
-    do {  // KT >= 1
-      // this wave's loads for this step landed (the previous tile's epilogue
-      // stores, issued after them, may still be in flight) ...
-      if (VEC && kt == 0 && !first)
-        __builtin_amdgcn_s_waitcnt(wait_epi(!EXACT));
-      else
-        __builtin_amdgcn_s_waitcnt(wait_step(!EXACT));
-      __builtin_amdgcn_s_barrier();  // ... and every other wave's
-      if (kt == 0) {
-        // the epilogue's column scales and biases, straight into LDS (no
-        // registers, so no wait on them lands before the epilogue): wave w
-        // fetches the scales of columns 64w .. 64w + 63, waves 0 and 1 the
-        // biases of 128 columns each, two per lane (columns past N: zeros,
-        // never stored)
-        const int nc = cur.n0 + wave * 64 + lane;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsw, (__attribute__((address_space(3))) void*)(Psc + __builtin_amdgcn_readfirstlane(wave * 64)), 4,
-            (int)(g.per_channel ? (nc < g.N ? (uint32_t)nc * 4 : kOutOfRange) : 0u), 0, 0, 0);
-        if (VEC && wave < 2) {  // N % 8 == 0: no dword straddles the end
-          const int nb2 = cur.n0 + wave * 128 + 2 * lane;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rbias, (__attribute__((address_space(3))) void*)(Pbias + __builtin_amdgcn_readfirstlane(wave * 128)),
-              4, (int)(nb2 < g.N ? (uint32_t)nb2 * 2 : kOutOfRange), 0, 0, 0);
-        }
-      }
-      const uint8_t* As = smem + (step & 1) * kStageBytes;
-      const uint8_t* Ws = As + kOperandBytes;
-      // next step's loads into the idle buffer: this tile's next step, or the
-      // next tile's first step (zeros after the last tile)
-      const bool last_step = kt + 1 >= KT;
-      Tile tgt;
-      tgt.ra = last_step ? nxt.ra : cur.ra;
-      tgt.rw = last_step ? nxt.rw : cur.rw;
-      const int k_next = last_step ? 0 : (kt + 1) * BK;
-      const bool v_next = last_step ? has_next : true;
-      const int nstage = (step + 1) & 1;
-      // order: the first half's fragments; then the first half's 16 products,
-      // each pair followed by one block of next-step loads and two of the
-      // second half's fragment reads; then the second half's products
-      v8i wf[2][4], af[2][4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wf[0][i] = read_frag(Ws, wn * 128 + i * 32 + frow, fchunk);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) af[0][j] = read_frag(As, wm * 128 + j * 32 + frow, fchunk);
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (!EXACT) {
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int i = (2 * p + q) >> 2, j = (2 * p + q) & 3;
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[0][i], af[0][j], acc[i][j], FW, FA,
-                                                                         0, 0, 0, 0);
-          }
-          dma_part(nstage, tgt, k_next, v_next, p);
-          if (p == 7) prefetch(cur, kt + kPrefetchDist, kt + kPrefetchDist < KT);
-          if (p < 4) wf[1][p] = read_frag(Ws, wn * 128 + p * 32 + frow, 4 + fchunk);
-          else af[1][p - 4] = read_frag(As, wm * 128 + (p - 4) * 32 + frow, 4 + fchunk);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[1][i], af[1][j], acc[i][j], FW, FA,
-                                                                         0, 0, 0, 0);
-      } else {
-        // the lane's 32 k-values in four slices of 8 (same slicing for
-        // both operands), one bf16 32x32x16 product per slice; two blocks of
-        // loads and two fragment reads after each slice of the first half
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            bf16x8 wb[4], ab[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) wb[i] = slice_bf16<FW>(wf[ks][i], t);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ab[j] = slice_bf16<FA>(af[ks][j], t);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-              for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb[i], ab[j], acc[i][j], 0, 0, 0);
-            if (ks == 0) {
-              dma_part(nstage, tgt, k_next, v_next, 2 * t);
-              dma_part(nstage, tgt, k_next, v_next, 2 * t + 1);
-              wf[1][t] = read_frag(Ws, wn * 128 + t * 32 + frow, 4 + fchunk);
-              af[1][t] = read_frag(As, wm * 128 + t * 32 + frow, 4 + fchunk);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-          }
-        }
-      }
-      ++step;
-    } while (++kt < KT);
+    if (KT == 1) {
+      do_step(True(), True(), cur, P);
+    } else {
+      do_step(True(), False(), cur, P);
+      for (int kt = 1; kt < KT - 1; ++kt) do_step(False(), False(), cur, P);
+      do_step(False(), True(), cur, P);
+    }
 
     // ---- epilogue.  acc[i][j] = D[n][m] for the 32x32 block (i: n, j: m):
     // lane holds m = lane % 32 and, in registers 4q..4q+3, the four
     // consecutive columns n = 8q + 4 * (lane / 32) + 0..3.  Each round parks
     // the 32 rows of block-row j (fp32, 512-byte LDS rows, 16-byte chunk c of
-    // row r at c ^ (r & 31)) in this wave's 16 KiB of the stage buffer the
-    // last step read, then reads them back as 8 columns per lane.
-    // every wave is done reading that buffer, and (for a single-step tile,
-    // whose scales no later step waited for) the scales have landed
-    if (KT == 1) __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __builtin_amdgcn_s_barrier();
-    float sc[8], bs[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      sc[e] = sa * Psc[ecol + e];
-      if constexpr (VEC)
-        bs[e] = bf16_to_f32(Pbias[ecol + e]);
-      else
-        bs[e] = g.bias ? bf16_to_f32(g.bias[min(cur.n0 + ecol + e, g.N - 1)]) : 0.0f;
+    // row r at c ^ r) in the last step's stage -- rows 0..15 in the 8 KiB of
+    // its A part and rows 16..31 in the 8 KiB of its W part that this wave's
+    // own loads fill, so no other wave touches them -- and reads them back
+    // as 8 consecutive columns per lane.
+    if (KT == 1) {
+      // a one-step tile: its parameter loads were issued this very step
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __builtin_amdgcn_s_barrier();
     }
-    float* E = reinterpret_cast<float*>(smem + ((step - 1) & 1) * kStageBytes + wave * 16384);
+    const int lstage = (step - 1) & 1;  // the stage the tile's last step read
+    uint8_t* const Spark = smem + lstage * kStageBytes;
+    float* const E0 = reinterpret_cast<float*>(Spark + wave * 8192);                   // rows 0..15
+    float* const E1 = reinterpret_cast<float*>(Spark + kOperandBytes + wave * 8192);   // rows 16..31
+    // The lane index, made opaque to the compiler here: the epilogue's
+    // per-lane LDS addresses and store offsets are loop-invariant, and
+    // hoisted out of the tile loop they would occupy (and spill) some sixty
+    // registers for the whole kernel.
+    int elane = lane;
+    asm volatile("" : "+v"(elane));
+    const int ec = elane & 15, er = (elane >> 4) & 3;  // read-back role: columns 8 ec .. + 7 of rows er + 4 s
+    const int ecol = wn * 128 + ec * 8;        // within the tile
+    const bool col_ok = cur.n0 + ecol + 8 <= g.N;
+    float sc[8], bs[8];
+    {
+      const float* Psc = reinterpret_cast<const float*>(P);
+      const uint16_t* Pbias = reinterpret_cast<const uint16_t*>(P + BN * 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sc[e] = sa * Psc[ecol + e];
+        if constexpr (VEC)
+          bs[e] = bf16_to_f32(Pbias[ecol + e]);
+        else
+          bs[e] = g.bias ? bf16_to_f32(g.bias[min(cur.n0 + ecol + e, g.N - 1)]) : 0.0f;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int r = lane & 31;
+      {
+        const int r = elane & 31;
+        float* const E = r < 16 ? E0 : E1;
+        const int rl = r & 15;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = i * 8 + 2 * q + (lane >> 5);
-          v4f v;
-          v[0] = acc[i][j][4 * q]; v[1] = acc[i][j][4 * q + 1];
-          v[2] = acc[i][j][4 * q + 2]; v[3] = acc[i][j][4 * q + 3];
-          *reinterpret_cast<v4f*>(E + r * 128 + ((c ^ r) << 2)) = v;
-        }
+          for (int q = 0; q < 4; ++q) {
+            const int c = i * 8 + 2 * q + ((elane >> 5) & 1);
+            v4f v;
+            v[0] = acc[i][j][4 * q]; v[1] = acc[i][j][4 * q + 1];
+            v[2] = acc[i][j][4 * q + 2]; v[3] = acc[i][j][4 * q + 3];
+            *reinterpret_cast<v4f*>(E + rl * 128 + ((c ^ r) << 2)) = v;
+          }
+      }
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int rr = s * 4 + er;
-        const v4f lo = *reinterpret_cast<const v4f*>(E + rr * 128 + (((2 * ec) ^ rr) << 2));
-        const v4f hi = *reinterpret_cast<const v4f*>(E + rr * 128 + (((2 * ec + 1) ^ rr) << 2));
+      for (int s8 = 0; s8 < 8; ++s8) {
+        const int rr = s8 * 4 + er;
+        const float* E = rr < 16 ? E0 : E1;
+        const int rl = rr & 15;
+        const v4f lo = *reinterpret_cast<const v4f*>(E + rl * 128 + (((2 * ec) ^ rr) << 2));
+        const v4f hi = *reinterpret_cast<const v4f*>(E + rl * 128 + (((2 * ec + 1) ^ rr) << 2));
         uint32_t o[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -422,11 +532,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
           }
         }
       }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       __builtin_amdgcn_wave_barrier();  // the next round rewrites E
     }
-    cur = nxt;
-    first = false;
+    // the deferred loads of the step after next go into this wave's own part
+    // of the stage it has just finished reading; then the next step's
+    // first-half fragments (their loads landed before the last barrier)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma_part(lstage, i);
+    advance_load();
+    if constexpr (!EXACT) prefetch();
+    {
+      const uint8_t* An = smem + (step & 1) * kStageBytes;
+      const uint8_t* Wn = An + kOperandBytes;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wf0[i] = read_frag(Wn, wn * 128 + i * 32 + frow, fchunk);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) af0[j] = read_frag(An, wm * 128 + j * 32 + frow, fchunk);
+    }
   }
+  // loads past the last tile still write (zeros) into LDS: let them land
+  // before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
 }
 
 int cu_count() {
