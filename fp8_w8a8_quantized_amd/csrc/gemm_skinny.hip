@@ -1,5 +1,4 @@
-// Skinny-M scaled FP8 GEMM for decode (M <= 64, 16 rows of M per workgroup),
-// gfx950.
+// Skinny-M scaled FP8 GEMM for decode (M <= 64), gfx950.
 //
 // "[WIP] FP8 support" (text-generation-inference PR 1484), review discussion:
 // decode runs at fewer than 16 rows, wants a dedicated GEMV-like kernel, and
@@ -37,10 +36,13 @@
 // torch._scaled_mm", description: the channelwise rescale follows the
 // per-tensor GEMM; fused here instead of a separate pass).
 //
-// M up to 64 runs the same kernels over a grid of 16-row blocks of M, and so
-// does any M for layouts the matrix-core GEMM does not take.  Layouts that
-// are not 16-byte aligned (or K % 16 != 0) use a byte-granular variant that
-// loads each lane's 32 bytes directly in the matrix-core layout.
+// M from 17 to 64 runs a multi-block variant in which one workgroup serves
+// every 16-row block of M (up to four) from each weight step, so the weight
+// still streams once; larger M on this path (layouts the matrix-core GEMM
+// does not take) uses grid rows of 64.  Layouts that are not 16-byte
+// aligned (or K % 16 != 0) use a byte-granular variant that loads each
+// lane's 32 bytes directly in the matrix-core layout, one 16-row block of M
+// per grid row.
 
 #include "device_common.h"
 #include "internal.h"
@@ -106,6 +108,21 @@ __device__ __forceinline__ v4f mfma_fp8_as_bf16(v8i wf, v8i af, v4f acc) {
     fp8x4_to_bf16<FA>(af[2 * t], ab, 0);
     fp8x4_to_bf16<FA>(af[2 * t + 1], ab, 4);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, ab, acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// As mfma_fp8_as_bf16 with the weight fragment already converted (wb[t]:
+// its k-values 8t..8t+7 as bf16), so one conversion serves several
+// activation blocks.
+template <int FA>
+__device__ __forceinline__ v4f mfma_bf16w_fp8a(const bf16x8 (&wb)[4], v8i af, v4f acc) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    bf16x8 ab;
+    fp8x4_to_bf16<FA>(af[2 * t], ab, 0);
+    fp8x4_to_bf16<FA>(af[2 * t + 1], ab, 4);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[t], ab, acc, 0, 0, 0);
   }
   return acc;
 }
@@ -189,6 +206,11 @@ __device__ __forceinline__ v8i cat8(v4i lo, v4i hi) {
 // 2^27 bytes, so every 16-byte chunk lies wholly inside or wholly outside
 // [0, K) and a 16-row block spans less than 2^31 bytes.
 constexpr int64_t kMaxPitch = int64_t(1) << 27;
+// 16-row blocks of M per workgroup of the multi-block kernel (one reducing
+// wave per block); its activation rows (up to 64) then span less than 2^31
+// bytes only for pitches below 2^25.
+constexpr int kMaxSkinnyBlocks = 4;
+constexpr int64_t kMaxPitchMB = int64_t(1) << 25;
 // Waves per workgroup and steps in flight per wave, measured on the decode
 // shapes of an 8B-class model (K = 4096 and 14336): deeper pipelines (3-8
 // steps) and 8 or 16 waves were slower, a single step in flight about as
@@ -445,6 +467,169 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny2_kernel(GemmArgs g) {
   reduce_and_store(g, acc1, red[1], NW, wave, lane, n0 + 16, m0, ep1);
 }
 
+// MB 16-row blocks of M per workgroup (M from 17 to 64 in one grid row,
+// larger M in grid rows of 16 * MB): each weight step a wave loads serves
+// every block, so the weight streams from HBM once per 16 * MB rows instead
+// of once per 16.  The pipeline is the one-block kernel's; each block has its
+// own activation staging buffer and accumulator, and the weight step is
+// transposed and its fragments read once for all blocks.  After the main
+// loop each wave parks its partial tiles in its own staging area and wave b
+// reduces and stores block b.
+template <int NW, int D, int MB, bool IL, bool NT, int FA, int FW>
+__global__ __launch_bounds__(NW * 64) void gemm_skinny_mb_kernel(GemmArgs g) {
+  static_assert(MB >= 1 && MB <= NW, "one reducing wave per block");
+  __shared__ __attribute__((aligned(16))) uint8_t stage[NW][1 + MB][16 * 256];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 15, grp = lane >> 4;
+  const int n0 = blockIdx.x * 16, m0 = blockIdx.y * (16 * MB);
+  const int steps = (g.K + 255) >> 8;
+  int first, stride, count;
+  if constexpr (IL) {
+    first = wave;
+    stride = NW;
+    count = max(steps - wave + NW - 1, 0) / NW;
+  } else {
+    const int per = (steps + NW - 1) / NW;
+    first = min(wave * per, steps);
+    stride = 1;
+    count = min(first + per, steps) - first;
+  }
+  const int lr = lane >> 4, lc = (lane & 15) * 16;
+  const int rows_w = min(g.N - n0, 16), rows_a = min(g.M - m0, 16 * MB);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.w + (int64_t)n0 * g.ldw), (short)0, (int)(rows_w * g.ldw), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.a + (int64_t)m0 * g.lda), (short)0, (int)(rows_a * g.lda), kRsrcWord3);
+  const uint32_t ldw = (uint32_t)g.ldw, lda = (uint32_t)g.lda;
+  uint32_t wo[4], ao[MB][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t row = 4 * j + lr;
+    wo[j] = (int)row < rows_w ? row * ldw + lc : kOutOfRange;
+#pragma unroll
+    for (int b = 0; b < MB; ++b) {
+      const uint32_t rowa = 16 * b + row;
+      ao[b][j] = (int)rowa < rows_a ? rowa * lda + lc : kOutOfRange;
+    }
+  }
+  uint8_t* LW = stage[wave][0];
+  const int swz_w = (lane & 15);
+
+  v4i wv[D][4], av[D][MB][4];
+  auto issue = [&](int slot, int i) {  // the wave's i-th step
+    const int k0 = (first + i * stride) * 256;
+    const bool kin = i < count && k0 + lc < g.K;
+    uint32_t ow[4], oa[MB][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ow[j] = kin ? wo[j] + k0 : kOutOfRange;
+#pragma unroll
+      for (int b = 0; b < MB; ++b) oa[b][j] = kin ? ao[b][j] + k0 : kOutOfRange;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      wv[slot][j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rw, ow[j], 0, NT ? kNonTemporal : 0));
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        av[slot][b][j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, oa[b][j], 0, 0));
+  };
+  constexpr int kLoads = 4 + 4 * MB;  // per step
+  __builtin_amdgcn_sched_barrier(0);
+  const EpiParams ep = load_epi_params(g, lane, n0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d) {
+    issue(d, d);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  v4f acc[MB];
+#pragma unroll
+  for (int b = 0; b < MB; ++b) acc[b] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < count; i += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      issue((d + D - 1) % D, i + d + D - 1);
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLoads * (D - 1)));
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + d < count) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = 4 * j + lr;
+          *reinterpret_cast<v4i*>(LW + row * 256 + ((swz_w ^ row) << 4)) = wv[d][j];
+#pragma unroll
+          for (int b = 0; b < MB; ++b)
+            *reinterpret_cast<v4i*>(stage[wave][1 + b] + row * 256 + ((swz_w ^ row) << 4)) = av[d][b][j];
+        }
+        // the same wave reads what its other lanes wrote: LDS operations of a
+        // wave complete in order, so waiting for them suffices
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int c0 = t * 8 + grp, c1 = t * 8 + 4 + grp;
+          const v8i wf = cat8(*reinterpret_cast<const v4i*>(LW + r * 256 + ((c0 ^ r) << 4)),
+                              *reinterpret_cast<const v4i*>(LW + r * 256 + ((c1 ^ r) << 4)));
+          bf16x8 wb[4];  // the weight fragment converted once for every block
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            fp8x4_to_bf16<FW>(wf[2 * u], wb[u], 0);
+            fp8x4_to_bf16<FW>(wf[2 * u + 1], wb[u], 4);
+          }
+#pragma unroll
+          for (int b = 0; b < MB; ++b) {
+            const uint8_t* LA = stage[wave][1 + b];
+            const v8i af = cat8(*reinterpret_cast<const v4i*>(LA + r * 256 + ((c0 ^ r) << 4)),
+                                *reinterpret_cast<const v4i*>(LA + r * 256 + ((c1 ^ r) << 4)));
+            acc[b] = mfma_bf16w_fp8a<FA>(wb, af, acc[b]);
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+  }
+  // partial tiles into this wave's own staging area (no other wave touches
+  // it), then wave b sums block b over the waves in wave order and stores it
+  float* mine = reinterpret_cast<float*>(stage[wave][0]);
+#pragma unroll
+  for (int b = 0; b < MB; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mine[(b * 4 + i) * 64 + lane] = acc[b][i];
+  __syncthreads();
+  if (wave >= MB) return;
+  const int b = wave;
+  float sum[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float t = reinterpret_cast<const float*>(stage[0][0])[(b * 4 + i) * 64 + lane];
+    for (int w = 1; w < NW; ++w) t += reinterpret_cast<const float*>(stage[w][0])[(b * 4 + i) * 64 + lane];
+    sum[i] = t;
+  }
+  const float sa = *g.s_a;
+  const int m = m0 + 16 * b + (lane & 15);
+  if (m >= g.M) return;
+  const int nb = n0 + 4 * grp;
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = f32_to_bf16_rne(__builtin_fmaf(sum[i], sa * ep.sw[i], bf16_to_f32(ep.bias[i])));
+  uint16_t* orow = g.out + (int64_t)m * g.ldo;
+  if (nb + 3 < g.N && ((uintptr_t)(orow + nb) % 8) == 0) {
+    uint2 v;
+    v.x = o[0] | (o[1] << 16);
+    v.y = o[2] | (o[3] << 16);
+    *reinterpret_cast<uint2*>(orow + nb) = v;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (nb + i < g.N) orow[nb + i] = (uint16_t)o[i];
+  }
+}
+
 template <int NW, int U, bool VEC, int FA, int FW>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_generic_kernel(GemmArgs g) {
   __shared__ float red[NW][4][64];
@@ -481,13 +666,43 @@ hipError_t launch_generic(const GemmArgs& g, dim3 grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Rows of M per grid row of the multi-block kernel.
+int skinny_rows_per_grid_row(const GemmArgs& g) { return 16 * min((g.M + 15) / 16, kMaxSkinnyBlocks); }
+
+template <int MB, int FA, int FW>
+hipError_t launch_mb(const GemmArgs& g, hipStream_t stream) {
+  const bool il = (g.K + 255) / 256 >= 32;
+  const bool nt = (int64_t)g.N * g.K >= (int64_t(32) << 20);
+  const dim3 grid((unsigned)((g.N + 15) / 16), (unsigned)((g.M + 16 * MB - 1) / (16 * MB)));
+  const dim3 block(kSkinnyWaves * 64);
+  if (il && nt)
+    gemm_skinny_mb_kernel<kSkinnyWaves, kSkinnyDepth, MB, true, true, FA, FW><<<grid, block, 0, stream>>>(g);
+  else if (il)
+    gemm_skinny_mb_kernel<kSkinnyWaves, kSkinnyDepth, MB, true, false, FA, FW><<<grid, block, 0, stream>>>(g);
+  else if (nt)
+    gemm_skinny_mb_kernel<kSkinnyWaves, kSkinnyDepth, MB, false, true, FA, FW><<<grid, block, 0, stream>>>(g);
+  else
+    gemm_skinny_mb_kernel<kSkinnyWaves, kSkinnyDepth, MB, false, false, FA, FW><<<grid, block, 0, stream>>>(g);
+  return hipGetLastError();
+}
+
+template <int FA, int FW>
+hipError_t launch_skinny_mb(const GemmArgs& g, hipStream_t stream) {
+  switch (skinny_rows_per_grid_row(g) / 16) {
+    case 2: return launch_mb<2, FA, FW>(g, stream);
+    case 3: return launch_mb<3, FA, FW>(g, stream);
+    default: return launch_mb<4, FA, FW>(g, stream);
+  }
+}
+
 template <int FA, int FW>
 hipError_t launch_skinny(const GemmArgs& g, hipStream_t stream) {
   const bool aligned = ((uintptr_t)g.a % 16 == 0) && ((uintptr_t)g.w % 16 == 0) && (g.lda % 16 == 0) &&
                        (g.ldw % 16 == 0) && (g.K % 16 == 0) && g.lda < kMaxPitch && g.ldw < kMaxPitch &&
-                       g.N < (1 << 29);
+                       g.N < (1 << 29) && (g.M <= 16 || g.lda < kMaxPitchMB);
   const int64_t tiles_n = (g.N + 15) / 16, tiles_m = (g.M + 15) / 16;
   dim3 grid((unsigned)tiles_n, (unsigned)tiles_m);
+  if (aligned && g.M > 16) return launch_skinny_mb<FA, FW>(g, stream);
   if (aligned) {
     // Interleaved steps for long K (>= 8192), contiguous ranges otherwise;
     // weights of 32 MiB and more streamed with non-temporal loads.  Each

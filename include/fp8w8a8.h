@@ -173,9 +173,11 @@ fp8_status fp8_quant_dynamic_per_row(const uint16_t* x_bf16, int64_t rows, int64
  *   bias   N bf16 values (device), or NULL for none
  *   out    [M, N] bf16, row pitch ldo >= N            (output)
  * M <= 64 runs the skinny (decode) kernel, which streams the weight once
- * with no padding or repacking; larger M runs the LDS-staged matrix-core
- * GEMM (and layouts it does not take -- rows not 16-byte aligned or
- * K % 16 != 0 -- the skinny kernel).  Any M, N, K >= 1 is accepted.
+ * (one workgroup serves all rows of M) with no padding or repacking; larger
+ * M runs the LDS-staged matrix-core GEMM (and layouts it does not take --
+ * rows not 16-byte aligned or K % 16 != 0 -- the skinny kernel, which then
+ * reads the weight once per 64 rows of M, or per 16 rows for unaligned
+ * layouts).  Any M, N, K >= 1 is accepted.
  * Errors: INVALID_ARG for null pointers (bias may be NULL), negative M or
  * N, K < 1, lda/ldw < K, ldo < N, or an unknown scale mode; UNSUPPORTED for
  * M or N >= 2^31, K >= 2^30 or pitches >= 2^40.  M == 0 or N == 0 is an

@@ -77,7 +77,7 @@ def _gemm_case(m, k, n, fa, fw, per_channel, accum, seed):
 
 
 @pytest.mark.parametrize("fa,fw", FMTS)
-@pytest.mark.parametrize("m,k,n", [(16, 4096, 1030), (3, 4096, 4100), (7, 1000, 33),
+@pytest.mark.parametrize("m,k,n", [(16, 4096, 1030), (3, 4096, 4100), (7, 1000, 33), (40, 4096, 300),
                                    # K >= 8192 (interleaved K steps) and/or >= 32 MiB of weights
                                    # (non-temporal loads): every variant of the skinny kernel
                                    (3, 8208, 257), (4, 8192, 4100), (5, 4096, 8200), (6, 2048, 16400)])

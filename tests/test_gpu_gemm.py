@@ -84,11 +84,14 @@ def test_skinny_tiny_and_ragged_k(m, k, n):
 
 # -------------------------------------------------- mid M (skinny over M blocks)
 @pytest.mark.parametrize("m,k,n", [(17, 4096, 1030), (33, 512, 4100), (64, 1024, 300),
-                                   (40, 14336, 2401), (20, 4096, 8200)])
+                                   (40, 14336, 2401), (20, 4096, 8200), (48, 1040, 777), (63, 8208, 513),
+                                   (57, 4096, 16)])
 def test_mid_m(m, k, n):
-    """16 < M <= 64 on the skinny kernel; the last two shapes have at least
-    32 MiB of weights (non-temporal loads), with interleaved and with
-    contiguous K steps, a ragged N and a partial last block of M."""
+    """16 < M <= 64 on the skinny kernel, every 16-row block of M in one
+    workgroup (two, three or four blocks); shapes with at least 32 MiB of
+    weights (non-temporal loads), interleaved and contiguous K steps, K
+    tails that are not whole 256-byte steps, a ragged N and a partial last
+    block of M."""
     say("mid m", m, k, n)
     d = _prepare(4, m, k, n, per_channel=False, with_bias=True)
     _run_and_check(d, False)
