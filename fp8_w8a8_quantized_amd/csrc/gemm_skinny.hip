@@ -44,6 +44,9 @@
 // lane's 32 bytes directly in the matrix-core layout, one 16-row block of M
 // per grid row.
 
+#include <algorithm>
+#include <atomic>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -234,6 +237,31 @@ constexpr int kNonTemporal = 2;
 // (two per CU): below that the wider workgroups leave CUs idle.
 constexpr int kTwoBlockMinGrid = 512;
 
+// Compute units of the current device (looked up once per device).
+int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Rows per workgroup of the two-block kernel: the fewest workgroups per CU
+// that 32-row workgroups would need, then rows (a multiple of 4) spread
+// evenly over that many workgroups per CU, so every CU gets the same number.
+// On the 4096 -> 28672 decode shape: 28 rows, 1024 workgroups (4 per CU),
+// 21.7 against 22.2 us with 32 rows (896 workgroups, 3 or 4 per CU).
+int two_block_rows(int64_t N) {
+  const int64_t cus = device_cus();
+  const int64_t per_cu = (N + 32 * cus - 1) / (32 * cus);
+  const int64_t rows = (N + cus * per_cu - 1) / (cus * per_cu);
+  return (int)std::min<int64_t>(32, (rows + 3) / 4 * 4);
+}
+
 template <int NW, int D, bool IL, bool NT, int FA, int FW>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[NW][2][16 * 256];
@@ -354,23 +382,23 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(GemmArgs g) {
 // on the 4096 -> 28672 decode shape, 23.3 -> 22.3 us against the one-block
 // kernel (two steps in flight take 221 VGPRs, two waves per SIMD, and lose
 // the gain).  The second block's weight step goes through the same staging
-// buffer once the first block's fragments are in registers.  Rows past N (a
-// last block past the end, or a partial one) read as zeros and are never
-// stored.
+// buffer once the first block's fragments are in registers.  A workgroup
+// covers wg_rows rows (a multiple of 4, at most 32); rows past those or past
+// N read as zeros and are never stored.
 template <int NW, int D, bool NT, int FA, int FW>
-__global__ __launch_bounds__(NW * 64) void gemm_skinny2_kernel(GemmArgs g) {
+__global__ __launch_bounds__(NW * 64) void gemm_skinny2_kernel(GemmArgs g, int wg_rows) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[NW][2][16 * 256];
   __shared__ float red[2][NW][4][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r = lane & 15, grp = lane >> 4;
-  const int n0 = blockIdx.x * 32, m0 = blockIdx.y * 16;
+  const int n0 = blockIdx.x * wg_rows, m0 = blockIdx.y * 16;
   const int steps = (g.K + 255) >> 8;
   const int per = (steps + NW - 1) / NW;
   const int first = min(wave * per, steps);
   const int count = min(first + per, steps) - first;
   const int lr = lane >> 4, lc = (lane & 15) * 16;
-  const int rows_w = min(g.N - n0, 32), rows_a = min(g.M - m0, 16);
+  const int rows_w = min(g.N - n0, wg_rows), rows_a = min(g.M - m0, 16);
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(g.w + (int64_t)n0 * g.ldw), (short)0, (int)(rows_w * g.ldw), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
@@ -463,8 +491,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny2_kernel(GemmArgs g) {
       }
     }
   }
-  reduce_and_store(g, acc0, red[0], NW, wave, lane, n0, m0, ep0);
-  reduce_and_store(g, acc1, red[1], NW, wave, lane, n0 + 16, m0, ep1);
+  GemmArgs gs = g;  // stores end at this workgroup's last row
+  gs.N = min(g.N, n0 + wg_rows);
+  reduce_and_store(gs, acc0, red[0], NW, wave, lane, n0, m0, ep0);
+  reduce_and_store(gs, acc1, red[1], NW, wave, lane, n0 + 16, m0, ep1);
 }
 
 // MB 16-row blocks of M per workgroup (M from 17 to 64 in one grid row,
@@ -714,11 +744,12 @@ hipError_t launch_skinny(const GemmArgs& g, hipStream_t stream) {
     const bool nt = (int64_t)g.N * g.K >= (int64_t(32) << 20);
     const dim3 block(kSkinnyWaves * 64);
     if (!il && (g.N + 31) / 32 >= kTwoBlockMinGrid) {
-      const dim3 grid2((unsigned)((g.N + 31) / 32), (unsigned)tiles_m);
+      const int rw = two_block_rows(g.N);
+      const dim3 grid2((unsigned)((g.N + rw - 1) / rw), (unsigned)tiles_m);
       if (nt)
-        gemm_skinny2_kernel<kSkinnyWaves, 1, true, FA, FW><<<grid2, block, 0, stream>>>(g);
+        gemm_skinny2_kernel<kSkinnyWaves, 1, true, FA, FW><<<grid2, block, 0, stream>>>(g, rw);
       else
-        gemm_skinny2_kernel<kSkinnyWaves, 1, false, FA, FW><<<grid2, block, 0, stream>>>(g);
+        gemm_skinny2_kernel<kSkinnyWaves, 1, false, FA, FW><<<grid2, block, 0, stream>>>(g, rw);
       return hipGetLastError();
     }
     if (il && nt)

@@ -56,10 +56,11 @@ def test_skinny_per_channel_llama_shapes(m, k, n):
 
 
 @pytest.mark.parametrize("m,k,n,pc", [(16, 4096, 16400, True), (3, 2048, 16392, False), (13, 1024, 16400, True),
-                                      (16, 4096, 28672, False)])
+                                      (16, 4096, 28672, False), (9, 4096, 20000, True), (16, 1024, 30000, False)])
 def test_skinny_large_n_ragged(m, k, n, pc):
-    """N of 16384 and more with K below 8192: a last 16-row block partly past
-    N, plain and non-temporal weight loads, per-tensor and channelwise."""
+    """N of 16384 and more with K below 8192 (two weight blocks per wave, 24,
+    28 or 32 rows per workgroup on 256 CUs): a last workgroup partly past N,
+    plain and non-temporal weight loads, per-tensor and channelwise."""
     say("skinny large n", m, k, n, pc)
     d = _prepare(6, m, k, n, per_channel=pc, rowmul=pc, with_bias=pc)
     _run_and_check(d, pc)
