@@ -137,6 +137,32 @@ def time_graph_per_launch(launch, n_launches, replays=3):
     return e0.elapsed_time(e1) * 1e-3 / (replays * n_launches)
 
 
+def time_eager_per_launch(launch, n_launches):
+    """Mean time per launch of n_launches calls made by launch() from Python
+    (one untimed pass first); HIP events on the launch stream."""
+    launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    launch()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / n_launches
+
+
+def copy_calibration(mib):
+    """A fill, a device copy (3 times) and a sum over a buffer of `mib` MiB:
+    kernels of known traffic, against which profiler byte counters are scaled."""
+    nb = mib << 20
+    src = torch.ones(nb, dtype=torch.uint8, device="cuda")   # fill: writes nb bytes
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)                                         # copy: reads and writes nb
+    total = src.view(torch.int32).sum()                        # reduction: reads nb
+    torch.cuda.synchronize()
+    del src, dst, total
+
+
 def time_steps(lin, ws, accum, steps, warmup, eager=False):
     """Wall time per step: each step's launches captured once per weight copy
     into a HIP graph and replayed (or launched eagerly)."""
@@ -226,7 +252,9 @@ def bench_skinny(args):
     once): 16 x 4096 -> 4096, and Mistral-7B-shaped GEMMs at M in {1, 3, 7,
     13} with N in {4096, 14336, 4100, 1030, 6144} (K = 4096) and 14336 -> 4096,
     plus M = 32 and 64 on the same shapes.  Each shape's weight rotates over
-    copies totalling at least 1 GiB, so it streams from HBM."""
+    copies totalling at least 1 GiB, so it streams from HBM.  A graph of one
+    launch per copy is timed (with --eager: the launches from Python, one
+    untimed pass first)."""
     log("building inputs: skinny GEMMs")
     pool = {}
     for j, (k, n) in enumerate(synth.MISTRAL_7B_KN):
@@ -251,7 +279,10 @@ def bench_skinny(args):
         def launch(copies=copies, a_q=a_q, s_a=s_a, out=out):
             for (w_q, s_w) in copies:
                 fp8.scaled_mm(a_q, w_q, s_a, s_w, False, out=out)
-        t = time_graph_per_launch(launch, len(copies))
+        if args.eager:
+            t = time_eager_per_launch(launch, len(copies))
+        else:
+            t = time_graph_per_launch(launch, len(copies))
         b = gemm_bytes(m, k, n, per_channel=False)
         rows.append({"M": m, "K": k, "N": n, "what": what, "us": round(t * 1e6, 2),
                      "GBps": round(b / t / 1e9, 1), "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4),
@@ -435,6 +466,8 @@ def main():
     if args.workload == "skinny":
         line = {"metric": METRIC + " -- small-M per-tensor GEMMs", "unit": "GB/s", "n_gpus": 1,
                 "higher_is_better": True, "data": "synthetic", "skinny": bench_skinny(args)}
+        if args.copy_calibration_mib > 0:
+            copy_calibration(args.copy_calibration_mib)
         line["value"] = round(float(np.mean([r["GBps"] for r in line["skinny"]["gemms"] if r["M"] <= 16])), 1)
         print(json.dumps(line), flush=True)
         return
@@ -456,14 +489,7 @@ def main():
     per_shape_s = gemm_times(lin, args.accum, reps)
 
     if args.copy_calibration_mib > 0:
-        nb = args.copy_calibration_mib << 20
-        src = torch.ones(nb, dtype=torch.uint8, device="cuda")   # fill: writes nb bytes
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)                                         # copy: reads and writes nb
-        total = src.view(torch.int32).sum()                        # reduction: reads nb
-        torch.cuda.synchronize()
-        del src, dst, total
+        copy_calibration(args.copy_calibration_mib)
 
     step_bytes = sum(quant_bytes(m, L["k"]) + gemm_bytes(m, L["k"], L["n"]) for L in lin)
     step_flops = sum(2 * m * L["k"] * L["n"] for L in lin)
