@@ -45,13 +45,21 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// float32 -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN).
-// Branch-free: both results are formed and one is selected.
+// float32 -> bf16 bits, round to nearest even: the language's conversion,
+// which gfx950 performs with v_cvt_pk_bf16_f32 (two values per instruction).
+// Measured on MI355X over all 2^32 float32 patterns: bit-identical to the
+// integer rounding (u + 0x7fff + ((u >> 16) & 1)) >> 16 on every non-NaN
+// input (denormals and infinities included); a NaN gives a NaN.
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  const uint32_t quiet_nan = (u >> 16) | 0x40u;
-  return (u & 0x7fffffffu) > 0x7f800000u ? quiet_nan : rounded;
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Two float32 -> a packed bf16 pair (a in the low half), rounded as above.
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float a, float b) {
+  bf16x2 v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Per-tensor scale from amax: amax / max(format) correctly rounded in

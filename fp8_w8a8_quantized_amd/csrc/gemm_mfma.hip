@@ -511,24 +511,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
         const int rl = rr & 15;
         const v4f lo = *reinterpret_cast<const v4f*>(E + rl * 128 + (((2 * ec) ^ rr) << 2));
         const v4f hi = *reinterpret_cast<const v4f*>(E + rl * 128 + (((2 * ec + 1) ^ rr) << 2));
-        uint32_t o[8];
+        // columns 8 ec + 0..7 as bf16 pairs (one conversion instruction each)
+        v4u packed;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          o[e] = f32_to_bf16_rne(__builtin_fmaf(lo[e], sc[e], bs[e]));
-          o[e + 4] = f32_to_bf16_rne(__builtin_fmaf(hi[e], sc[e + 4], bs[e + 4]));
+        for (int e = 0; e < 2; ++e) {
+          packed[e] = pack_bf16x2_rne(__builtin_fmaf(lo[2 * e], sc[2 * e], bs[2 * e]),
+                                      __builtin_fmaf(lo[2 * e + 1], sc[2 * e + 1], bs[2 * e + 1]));
+          packed[e + 2] = pack_bf16x2_rne(__builtin_fmaf(hi[2 * e], sc[2 * e + 4], bs[2 * e + 4]),
+                                          __builtin_fmaf(hi[2 * e + 1], sc[2 * e + 5], bs[2 * e + 5]));
         }
         const int row = wm * 128 + j * 32 + rr;  // within the tile
         if constexpr (VEC) {
-          v4u packed;
-          packed[0] = o[0] | (o[1] << 16); packed[1] = o[2] | (o[3] << 16);
-          packed[2] = o[4] | (o[5] << 16); packed[3] = o[6] | (o[7] << 16);
           const uint32_t off = col_ok ? (uint32_t)((row * g.ldo + ecol) * 2) : kOutOfRange;
           __builtin_amdgcn_raw_buffer_store_b128(packed, cur.ro, (int)off, 0, 0);
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const uint32_t off = ecol + e < cur.cols ? (uint32_t)((row * g.ldo + ecol + e) * 2) : kOutOfRange;
-            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)o[e], cur.ro, (int)off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(packed[e >> 1] >> (16 * (e & 1))), cur.ro, (int)off, 0,
+                                                  0);
           }
         }
       }

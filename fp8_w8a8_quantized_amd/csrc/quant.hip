@@ -121,7 +121,7 @@ __device__ __forceinline__ v4i pack8_bf16_f64(const double f[8]) {
 __device__ __forceinline__ v4i pack8_bf16(const float f[8]) {
   v4i v;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = (int)(f32_to_bf16_rne(f[2 * i]) | (f32_to_bf16_rne(f[2 * i + 1]) << 16));
+  for (int i = 0; i < 4; ++i) v[i] = (int)pack_bf16x2_rne(f[2 * i], f[2 * i + 1]);
   return v;
 }
 
