@@ -47,3 +47,42 @@ def test_noalloc_matches_workspace_entry_point_twice(first, second):
     for i, (m, k, n, pc) in enumerate((first, second)):
         say(f"noalloc call {i}: {m} x {k} -> {n} {'channelwise' if pc else 'per tensor'}")
         _case(40 + i, m, k, n, pc)
+
+
+@pytest.mark.parametrize("m,k,n", [(16, 4096, 1030), (16, 14336, 512), (300, 1024, 520)])
+def test_noalloc_captured_in_a_graph(m, k, n):
+    """The callers this entry point is for capture it into HIP graphs: one
+    capture, four replays with eager work between them (output clears, a new
+    input), each replay bit-identical to the workspace entry point called
+    eagerly on the same input."""
+    say("noalloc graph", m, k, n)
+    w_q, s_w = fp8.quant_weight(dev_bf16(synth.weights(44, n, k, row_multipliers=True)), True)
+    bd = dev_bf16(synth.bias(44, n))
+    x = dev_bf16(synth.activations(44, m, k, outliers=True))
+    x2 = dev_bf16(synth.activations(45, m, k, outliers=False, scale=3.0))
+    a_q = torch.empty((m, k), dtype=torch.uint8, device="cuda")
+    s_a = torch.empty(1, dtype=torch.float32, device="cuda")
+    out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    for _ in range(2):  # warm up outside the capture
+        fp8.linear_dynamic_noalloc(x, w_q, s_w, True, bd, a_q, s_a, out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fp8.linear_dynamic_noalloc(x, w_q, s_w, True, bd, a_q, s_a, out)
+    torch.cuda.synchronize()
+    ws = fp8.new_linear_workspace()
+    refs = []
+    for xi in (x, x2):
+        o, q, s = fp8.linear_dynamic(xi, w_q, s_w, True, bd, workspace=ws)
+        torch.cuda.synchronize()
+        refs.append((o.clone(), q.clone(), s.clone()))
+    x_orig = x.clone()
+    for rep in range(4):
+        a_q.zero_(); s_a.zero_(); out.zero_()
+        x.copy_(x2 if rep >= 2 else x_orig)  # the graph reads whatever the buffer holds
+        g.replay()
+        torch.cuda.synchronize()
+        want = refs[1] if rep >= 2 else refs[0]
+        assert torch.equal(out.view(torch.int16), want[0].view(torch.int16)), rep
+        assert torch.equal(a_q, want[1]), rep
+        assert torch.equal(s_a, want[2]), rep
