@@ -155,3 +155,25 @@ def test_quant_is_deterministic():
     q2, s2 = fp8.quant_dynamic(x)
     torch.cuda.synchronize()
     assert torch.equal(q1, q2) and torch.equal(s1, s2)
+
+
+@pytest.mark.parametrize("shape", [(32, 4096), (32, 4104), (1, 131072), (1, 131080), (2, 65544), (16, 8192)])
+@pytest.mark.parametrize("where", ["first", "last"])
+def test_dynamic_one_and_two_launch_boundary(shape, where):
+    """Either side of the one-launch limit (16384 units of 8 elements: 32 x 4096
+    and 1 x 131072 take one launch, one unit more takes two), with the tensor's
+    largest magnitude planted at its first or its last element, so the scale
+    depends on the slot or block that holds it."""
+    say("quant boundary", shape, where)
+    x = synth.activations(9, *shape, outliers=False).copy()
+    big = np.uint16(0xC2A0)  # bf16 -80.0, larger in magnitude than any generated value
+    if where == "first":
+        x[0, 0] = big
+    else:
+        x[-1, -1] = big
+    q, s = fp8.quant_dynamic(dev_bf16(x))
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_dynamic(x)
+    assert s_ref == np.float32(80.0) / np.float32(448.0)
+    assert host_f32(s)[0] == s_ref
+    assert np.array_equal(host_u8(q), q_ref)
