@@ -120,21 +120,27 @@ def run_step(lin, it, ws, accum):
         fp8.scaled_mm(L["a_q"], w_q, L["s_a"], s_w, True, out=L["out"], accum=accum)
 
 
-def time_graph_per_launch(launch, n_launches, replays=3):
+def time_graph_per_launch(launch, n_launches, replays=3, windows=1):
     """Mean time per launch of a graph holding n_launches back-to-back calls
-    made by launch(); HIP events on the stream the launches run on."""
+    made by launch(); HIP events on the stream the launches run on.  With
+    windows > 1 the timed replays are repeated in that many windows and the
+    median window's mean is returned (one slow window, e.g. a clock change
+    right after other work, does not decide the figure)."""
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         launch()
     g.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(replays):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e-3 / (replays * n_launches)
+    means = []
+    for _ in range(windows):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        means.append(e0.elapsed_time(e1) * 1e-3 / (replays * n_launches))
+    return float(np.median(means))
 
 
 def time_eager_per_launch(launch, n_launches):
@@ -196,10 +202,10 @@ def time_steps(lin, ws, accum, steps, warmup, eager=False):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
-def gemm_times(lin, accum, reps):
+def gemm_times(lin, accum, reps, windows=5):
     """Per-launch GEMM time of each linear: a graph of back-to-back GEMM
     launches over the weight copies (the activation codes and scale from the
-    last step)."""
+    last step), timed in `windows` windows of 3 replays (the median window)."""
     out = []
     for L in lin:
         rotate = len(L["copies"])
@@ -208,7 +214,7 @@ def gemm_times(lin, accum, reps):
             for _ in range(reps):
                 for (w_q, s_w) in L["copies"]:
                     fp8.scaled_mm(L["a_q"], w_q, L["s_a"], s_w, True, out=L["out"], accum=accum)
-        out.append(time_graph_per_launch(launch, reps * rotate))
+        out.append(time_graph_per_launch(launch, reps * rotate, windows=windows))
     return out
 
 
