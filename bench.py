@@ -302,6 +302,107 @@ def bench_skinny(args):
             "mean_frac_hbm_m_le_16": round(float(np.mean([r["frac_hbm"] for r in hbm])), 4)}
 
 
+def bench_next(args):
+    """The calls beyond the headline path, each timed like the GEMMs (a graph
+    of back-to-back calls, the median of five timed windows): the
+    producer-fused quantizations (residual add + RMS norm, SiLU*mul), the
+    static activation quantization and the weight quantization on the device,
+    at decode and prefill sizes of the Llama-3-8B layer; and e5m2 GEMMs (e5m2
+    activations and weights, channelwise, exact sums), at decode size with
+    weights rotated over 8 copies and at prefill size."""
+    log("building inputs: next rows")
+    bf = lambda bits: synth.bf16_bits_to_torch(bits).cuda()
+    dev = "cuda"
+    calls = []
+
+    def timed(fn, n):
+        def launch():
+            for _ in range(n):
+                fn()
+        return time_graph_per_launch(launch, n, windows=5)
+
+    def hbm_row(call, m, k, t, b, extra=None):
+        r = {"call": call, "M": m, "K": k, "us": round(t * 1e6, 2), "GBps": round(b / t / 1e9, 1),
+             "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4), "algorithmic_bytes": int(b)}
+        r.update(extra or {})
+        calls.append(r)
+
+    d_ff = 14336
+    for m in (16, PREFILL_M):
+        n = 16 if m == 16 else 2
+        h, d = bf(synth.activations(2, m, 4096, layer=7, outliers=True)), bf(synth.activations(2, m, 4096, layer=8))
+        ho = torch.empty_like(h)
+        q = torch.empty((m, d_ff), dtype=torch.uint8, device=dev)
+        s = torch.empty(1, dtype=torch.float32, device=dev)
+        nws = fp8.norm_workspace(m, dev)
+        qa = q[:, :4096]
+        t = timed(lambda: fp8.add_rmsnorm_quant(h, d, h_out=ho, q=qa, scale=s, workspace=nws), n)
+        hbm_row("add_rmsnorm_quant (bf16 h + delta in, h' and e4m3 codes out)", m, 4096, t, m * 4096 * 7 + 4)
+        sc = torch.tensor([0.05], dtype=torch.float32, device=dev)
+        t = timed(lambda: fp8.quant_static(h, sc, q=qa), n)
+        hbm_row("quant_static (bf16 in, e4m3 codes out)", m, 4096, t, m * 4096 * 3)
+        del h, d, ho
+        gu = bf(synth.activations(2, m, 2 * d_ff, layer=9, outliers=True))
+        ws = fp8.new_workspace(dev)
+        t = timed(lambda: fp8.silu_mul_quant(gu, q=q, scale=s, workspace=ws), n)
+        hbm_row("silu_mul_quant (bf16 gate|up in, e4m3 codes out)", m, d_ff, t, m * d_ff * 5 + 4)
+        del gu, q
+        torch.cuda.empty_cache()
+    for sub, (name, k, nn) in enumerate(synth.LLAMA3_8B_LINEARS):
+        w = synth.weights_device(2, nn, k, sub=sub, row_multipliers=True)
+        wq = torch.empty((nn, k), dtype=torch.uint8, device=dev)
+        sw = torch.empty(nn, dtype=torch.float32, device=dev)
+        t = timed(lambda: fp8.quant_dynamic_per_row(w, q=wq, scales=sw), 2)
+        hbm_row("weight quantization per output channel (bf16 in, e4m3 codes and scales out)", nn, k, t,
+                nn * k * 3 + 4 * nn, {"shape": name})
+        del w, wq, sw
+        torch.cuda.empty_cache()
+
+    # e5m2 GEMMs: codes of the decode and prefill activations and the layer's weights in e5m2
+    gemms = []
+    for sub, (name, k, nn) in enumerate(synth.LLAMA3_8B_LINEARS):
+        w = synth.weights_device(2, nn, k, sub=sub, row_multipliers=True)
+        w_q, s_w = fp8.quant_weight(w, per_channel=True, fmt="e5m2")
+        del w
+        copies = [(w_q, s_w)] + [(w_q.clone(), s_w.clone()) for _ in range(ROTATE_DECODE - 1)]
+        for m in (16, PREFILL_M):
+            x = bf(synth.activations(2 if m == 16 else 3, m, k, sub=sub, outliers=True))
+            a_q, s_a = fp8.quant_dynamic(x, fmt="e5m2")
+            del x
+            out = torch.empty((m, nn), dtype=torch.bfloat16, device=dev)
+            use = copies if m == 16 else copies[:1]
+            reps = 2 if m == 16 else 3
+
+            def launch(use=use, a_q=a_q, s_a=s_a, out=out, reps=reps):
+                for _ in range(reps):
+                    for (wq_, sw_) in use:
+                        fp8.scaled_mm(a_q, wq_, s_a, sw_, True, out=out, fmt_a="e5m2", fmt_w="e5m2")
+            t = time_graph_per_launch(launch, reps * len(use), windows=5)
+            r = {"M": m, "K": k, "N": nn, "shape": name, "us": round(t * 1e6, 2)}
+            if m == 16:
+                b = gemm_bytes(m, k, nn)
+                r.update({"GBps": round(b / t / 1e9, 1), "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4)})
+            else:
+                tf = 2 * m * k * nn / t / 1e12
+                r.update({"TFLOPs": round(tf, 1), "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
+                          "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)})
+            gemms.append(r)
+            del a_q, out
+        del copies, w_q, s_w
+        torch.cuda.empty_cache()
+    dec = [g for g in gemms if g["M"] == 16]
+    pre = [g for g in gemms if g["M"] != 16]
+    dec_b = sum(gemm_bytes(16, g["K"], g["N"]) for g in dec)
+    pre_f = sum(2 * g["M"] * g["K"] * g["N"] for g in pre)
+    return {"workload": "the calls beyond the headline path at the Llama-3-8B layer's sizes (decode M=16, prefill "
+                        "M=16384): producer-fused quantizations, static activation quantization, per-channel weight "
+                        "quantization, e5m2 x e5m2 GEMMs (channelwise, exact sums); synthetic inputs",
+            "quantizations": calls,
+            "e5m2_gemms": gemms,
+            "e5m2_decode_GBps": round(dec_b / (sum(g["us"] for g in dec) * 1e-6) / 1e9, 1),
+            "e5m2_prefill_TFLOPs": round(pre_f / (sum(g["us"] for g in pre) * 1e-6) / 1e12, 1)}
+
+
 def cpu_baseline(m, lin_shapes, row_frac=8, budget_s=8.0, threads=None):
     """Time the CPU oracle on a bounded sample of the same workload.
 
@@ -445,10 +546,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", choices=["all", "decode", "prefill", "skinny", "chain"], default="all",
+    ap.add_argument("--workload", choices=["all", "decode", "prefill", "skinny", "chain", "next"], default="all",
                     help="all (default): the decode line with prefill (both accumulation modes) and skinny "
                          "objects added; decode / prefill: that workload alone as the headline; skinny: the "
-                         "small-M per-tensor GEMMs alone; chain: the 32-layer Llama-3-8B-shaped stack, "
+                         "small-M per-tensor GEMMs alone; next: the producer-fused, static and weight "
+                         "quantizations and e5m2 GEMMs alone; chain: the 32-layer Llama-3-8B-shaped stack, "
                          "16 x 1024-token prefill, then decode steps at M=16 (--steps of them, default 512)")
     ap.add_argument("--accum", choices=["fp32", "fp8"], default="fp32",
                     help="GEMM accumulation of the decode / prefill / chain workloads: fp32-class sums (default) "
@@ -469,6 +571,12 @@ def main():
     if args.workload == "chain":
         return run_chain(args)
     torch.cuda.set_device(0)
+    if args.workload == "next":
+        line = {"metric": METRIC + " -- calls beyond the headline path", "unit": "GB/s", "n_gpus": 1,
+                "higher_is_better": True, "data": "synthetic", "next": bench_next(args)}
+        line["value"] = line["next"]["e5m2_decode_GBps"]
+        print(json.dumps(line), flush=True)
+        return
     if args.workload == "skinny":
         line = {"metric": METRIC + " -- small-M per-tensor GEMMs", "unit": "GB/s", "n_gpus": 1,
                 "higher_is_better": True, "data": "synthetic", "skinny": bench_skinny(args)}
@@ -541,6 +649,7 @@ def main():
         del lin
         torch.cuda.empty_cache()
         line["skinny"] = bench_skinny(args)
+        line["next"] = bench_next(args)
     else:
         del lin
         torch.cuda.empty_cache()

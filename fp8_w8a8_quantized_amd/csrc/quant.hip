@@ -425,16 +425,17 @@ __global__ __launch_bounds__(256) void quant_per_row_kernel(QuantArgs a, PlainSr
 // (float32 add, one rounding; written to h_out when d is given), then
 // inv_rms[row] = 1 / sqrt(sum(h'^2) / cols + eps) in float64 (the sum runs in
 // a fixed order: per-thread units in order, then a fixed butterfly and wave
-// order, so it is deterministic), then max |y| over y = bf16(h' * inv_rms),
-// formed exactly as NormSrc forms it (each thread reads back only the units
-// it wrote itself).  partial[b] = the workgroup's max, as bf16 magnitude
-// bits: the quantization pass folds these maxima, so every normalized value
-// is evaluated twice in all, not once per workgroup.
+// order, so it is deterministic), then max |y| over y = bf16(h' * inv_rms).
+// The float64 -> bf16 rounding is monotone and symmetric, so that maximum is
+// the rounding of the row's largest |h'| times inv_rms: y is not evaluated
+// here.  partial[b] = the workgroup's max, as bf16 magnitude bits: the
+// quantization pass folds these maxima and evaluates every y once.
 __global__ __launch_bounds__(256) void norm_rows_kernel(const uint16_t* h, int64_t ld_h, const uint16_t* d,
                                                         int64_t ld_d, uint16_t* h_out, int64_t ld_ho, uint32_t rows,
                                                         uint32_t cols, uint32_t units_per_row, double eps, bool vec,
                                                         double* inv_rms, uint32_t* partial) {
   __shared__ double wsum[4];
+  __shared__ uint32_t wmax[4];
   __shared__ uint32_t red[16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t m = 0;
@@ -443,6 +444,7 @@ __global__ __launch_bounds__(256) void norm_rows_kernel(const uint16_t* h, int64
     const uint16_t* drow = d ? d + (int64_t)r * ld_d : nullptr;
     uint16_t* orow = d ? h_out + (int64_t)r * ld_ho : nullptr;
     double acc = 0.0;
+    uint32_t hmax = 0;  // largest |h'| of the row, as bf16 magnitude bits
     for (uint32_t u = threadIdx.x; u < units_per_row; u += blockDim.x) {
       const uint32_t c0 = u * 8;
       v4i hv = load8_bf16(hrow, c0, cols, vec);
@@ -459,24 +461,26 @@ __global__ __launch_bounds__(256) void norm_rows_kernel(const uint16_t* h, int64
         const double x = bf16_at(hv, i);
         acc = __builtin_fma(x, x, acc);
       }
+      hmax = max(hmax, absmax_bits8(hv));
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    if (lane == 0) wsum[wave] = acc;
+    hmax = wave_max_u32(hmax);
+    if (lane == 0) {
+      wsum[wave] = acc;
+      wmax[wave] = hmax;
+    }
     __syncthreads();
     double t = 0.0;
-    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += wsum[w];
+    uint32_t hm = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+      t += wsum[w];
+      hm = max(hm, wmax[w]);
+    }
     const double g = 1.0 / sqrt(t / (double)cols + eps);
     if (threadIdx.x == 0) inv_rms[r] = g;
-    const uint16_t* srow = d ? orow : hrow;
-    for (uint32_t u = threadIdx.x; u < units_per_row; u += blockDim.x) {
-      const v4i hv = load8_bf16(srow, u * 8, cols, vec);
-      double f[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) f[i] = (double)bf16_at(hv, i) * g;
-      m = max(m, absmax_bits8(pack8_bf16_f64(f)));
-    }
-    __syncthreads();  // wsum is rewritten for the next row
+    m = max(m, f64_to_bf16_rne((double)bf16_to_f32(hm) * g) & 0x7fffu);
+    __syncthreads();  // wsum and wmax are rewritten for the next row
   }
   m = block_max_u32(m, red);
   if (threadIdx.x == 0) partial[blockIdx.x] = m;
