@@ -9,7 +9,9 @@ import pytest
 import torch
 
 import oracle
+import oracle.glue
 from oracle.w8a8 import bf16_bits_to_f32
+from fp8_w8a8_quantized_amd import synth
 
 
 def _bits_of(values_f32):
@@ -134,3 +136,27 @@ def test_ulp_distance():
     a = _bits_of([1.0, -1.0, 0.0])
     b = _bits_of([1.0078125, -1.0078125, -0.0])
     assert list(oracle.bf16_ulp_distance(a, b)) == [1, 1, 0]
+
+
+def test_bf16_rounding_is_monotone_and_symmetric_so_row_max_commutes():
+    """The statistics pass of the fused normalization takes a row's largest
+    |y| = |bf16(h' * g)| as bf16(max |h'| * g): that holds because rounding to
+    nearest is non-decreasing and odd.  Checked on sorted random doubles
+    (including exact bf16 midpoints and their neighbours) and on rows."""
+    rng = np.random.default_rng(12)
+    mids = []
+    for e in range(-20, 20):  # exact midpoints between consecutive bf16 values, and one ulp either side
+        m = rng.integers(128, 256, 64).astype(np.float64)
+        mid = (m + 0.5) * 2.0 ** (e - 7)
+        mids += [mid, np.nextafter(mid, 0), np.nextafter(mid, np.inf)]
+    x = np.sort(np.concatenate([rng.standard_normal(200000) * 10.0 ** rng.uniform(-6, 6, 200000)] + mids))
+    r = oracle.bf16_bits_to_f32(oracle.glue.f64_to_bf16_bits(x)).astype(np.float64)
+    assert np.all(np.diff(r) >= 0)
+    neg = oracle.bf16_bits_to_f32(oracle.glue.f64_to_bf16_bits(-x)).astype(np.float64)
+    assert np.array_equal(neg, -r)
+    for _ in range(50):
+        h = synth.activations(int(rng.integers(1, 1000)), 1, int(rng.integers(1, 5000)), outliers=True)
+        hx = oracle.bf16_bits_to_f32(h).astype(np.float64)
+        g = 1.0 / np.sqrt(np.mean(hx * hx) + 1e-5)
+        ymax = np.max(oracle.glue.f64_to_bf16_bits(hx * g) & 0x7FFF)
+        assert ymax == (oracle.glue.f64_to_bf16_bits(np.max(np.abs(hx)) * g) & 0x7FFF)
