@@ -92,3 +92,40 @@ def test_producers_empty():
     q2, s2, _ = fp8.silu_mul_quant(gu)
     torch.cuda.synchronize()
     assert host_f32(s)[0] == 1.0 and host_f32(s2)[0] == 1.0
+
+
+def _chunked_ref(fn, rows, chunk=1024):
+    """The oracle's bf16 output of fn(row range) over all rows, in chunks of
+    rows (bounded host memory), as one array."""
+    return np.concatenate([fn(r0, min(r0 + chunk, rows)) for r0 in range(0, rows, chunk)])
+
+
+@pytest.mark.parametrize("which", ["add_rmsnorm", "silu_mul"])
+def test_producers_at_prefill_size(which):
+    """The fused producers at the prefill sizes the benchmark times (16384 x
+    4096 normalization with a residual add; 16384 x 14336 SiLU*mul): the
+    scale over the whole tensor, h' and the codes on sampled rows plus the
+    last 64, bit for bit."""
+    m = 16384
+    rows = np.unique(np.concatenate([np.random.default_rng(7).integers(0, m, 96), np.arange(m - 64, m)]))
+    if which == "add_rmsnorm":
+        k = 4096
+        say("add_rmsnorm_quant at", m, "x", k)
+        h = synth.activations(44, m, k, outliers=True)
+        d = synth.activations(45, m, k, outliers=False)
+        hd, dd = dev_bf16(h), dev_bf16(d)
+        q, s, h2, _ = fp8.add_rmsnorm_quant(hd, dd, h_out=torch.empty_like(hd))
+        torch.cuda.synchronize()
+        h_ref = oracle.add_bf16(h, d)
+        assert np.array_equal(host_bf16_bits(h2)[rows], h_ref[rows])
+        y_ref = _chunked_ref(lambda a, b: oracle.rmsnorm(h_ref[a:b], 1e-5), m)
+    else:
+        k = 14336
+        say("silu_mul_quant at", m, "x", k)
+        gu = synth.activations(46, m, 2 * k, outliers=True)
+        q, s, _ = fp8.silu_mul_quant(dev_bf16(gu))
+        torch.cuda.synchronize()
+        y_ref = _chunked_ref(lambda a, b: oracle.silu_mul(gu[a:b], k), m)
+    s_ref = oracle.scale_from_amax(oracle.amax(oracle.bf16_bits_to_f32(y_ref)))
+    assert host_f32(s)[0] == s_ref
+    assert np.array_equal(host_u8(q)[rows], oracle.quant_static(y_ref[rows], s_ref))
