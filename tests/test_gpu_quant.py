@@ -177,3 +177,28 @@ def test_dynamic_one_and_two_launch_boundary(shape, where):
     assert s_ref == np.float32(80.0) / np.float32(448.0)
     assert host_f32(s)[0] == s_ref
     assert np.array_equal(host_u8(q), q_ref)
+
+
+@pytest.mark.parametrize("n,k", [(28672, 4096), (4096, 14336)])
+def test_per_channel_weight_quant_full_llama_shapes(n, k):
+    """Per-output-channel weight quantization at the two largest Llama-3-8B
+    shapes the benchmark times, codes and scales bit for bit."""
+    say("weight quant per channel", n, k)
+    w = synth.weights(2, n, k, row_multipliers=True)
+    q, s = fp8.quant_weight(dev_bf16(w), True)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_weight(w, True)
+    assert np.array_equal(host_f32(s), s_ref)
+    assert np.array_equal(host_u8(q), q_ref)
+
+
+def test_static_quant_prefill_size():
+    """Static quantization at the prefill size the benchmark times (16384 x
+    4096, the benchmark's scale 0.05): every code bit for bit, saturation
+    included."""
+    say("static quant 16384 x 4096")
+    x = synth.activations(3, 16384, 4096, outliers=True)
+    s = torch.tensor([0.05], dtype=torch.float32, device="cuda")
+    q = fp8.quant_static(dev_bf16(x), s)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u8(q), oracle.quant_static(x, np.float32(0.05)))
