@@ -129,6 +129,24 @@ def test_mfma_gemm_k_not_multiple_of_128(accum):
     _run_and_check(d, True, accum=accum)
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("m,n", [(13, 130), (40, 72), (300, 520)])
+def test_longest_k_the_oracle_sums_exactly(m, n):
+    """K = 131072, near the oracle's exactness limit (K < 171,196).  It
+    exercises the skinny kernel's longest interleaved K loop (M = 13, one
+    block of M; M = 40, three blocks per weight step), the matrix-core
+    kernel with 1,024 k steps per tile in both accumulation modes, and the
+    two-launch quantizer over up to 39 M elements.  The float32 sums round
+    once per matrix-core product (32 or 64 k at a time), a few thousand
+    times per output, far inside the tolerance."""
+    k = 131072
+    say("longest K", m, k, n)
+    d = _prepare(8, m, k, n, per_channel=True, outliers=True, rowmul=True, with_bias=True)
+    for accum in (("fp32", "fp8") if m > 64 else ("fp32",)):
+        say("  accumulation", accum)
+        _run_and_check(d, True, accum=accum)
+
+
 @pytest.mark.parametrize("m", [16, 300])
 @pytest.mark.parametrize("accum", ["fp32", "fp8"])
 def test_every_code_through_identity_weight(m, accum):
