@@ -129,6 +129,33 @@ def test_mfma_gemm_k_not_multiple_of_128(accum):
     _run_and_check(d, True, accum=accum)
 
 
+def test_m_above_64_with_a_weight_pitch_the_matrix_core_kernel_refuses():
+    """M = 80 with W rows 2^23 + 16 bytes apart: a 256-row weight panel would
+    span 2 GiB, past the matrix-core kernel's 32-bit buffer offsets, so the
+    multi-block skinny kernel runs M in two grid rows of 64 (the second one
+    partly past M).  Only the first K bytes of each weight row are codes."""
+    m, k, n, ldw = 80, 4096, 24, (1 << 23) + 16
+    say("pitched weight, M > 64", m, k, n, ldw)
+    d = _prepare(9, m, k, n, per_channel=True, outliers=True, rowmul=True, with_bias=True)
+    buf = torch.zeros((n, ldw), dtype=torch.uint8, device="cuda")
+    buf[:, :k].copy_(d["w_q"])
+    d["w_q"] = buf[:, :k]
+    assert d["w_q"].stride(0) == ldw
+    _run_and_check(d, True)
+    del buf
+
+
+@pytest.mark.timeout(600)
+def test_m_over_one_skinny_grid_slice():
+    """M = 1,048,580 rows with K = 24 (not a multiple of 16, so the
+    byte-granular skinny kernel): the rows go out in slices of 65535 blocks
+    of 16 (the grid's second dimension), here two, the second of 20 rows."""
+    m, k, n = 65535 * 16 + 20, 24, 40
+    say("two skinny slices", m, k, n)
+    d = _prepare(10, m, k, n, per_channel=True, rowmul=True, with_bias=True)
+    _run_and_check(d, True)
+
+
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("m,n", [(13, 130), (40, 72), (300, 520)])
 def test_longest_k_the_oracle_sums_exactly(m, n):
