@@ -157,6 +157,48 @@ def test_m_over_one_skinny_grid_slice():
 
 
 @pytest.mark.timeout(600)
+def test_activation_codes_past_4_gib_sampled_rows():
+    """A = 262,221 x 16,384 codes (4.3 GB): the matrix-core kernel's tiles
+    start past 2 and 4 GiB of A, so their base addresses need 64 bits.  The
+    bf16 activation is drawn on the device (N(0,1), -80 planted last, so the
+    scale is fl32(80/448)); the oracle quantizes the sampled rows itself from
+    their bf16 values, and the GPU's codes of those rows must equal its own.
+    The GEMM is checked on rows around the 2 and 4 GiB marks, the first and
+    the last (ragged) tile, in both accumulation modes."""
+    m, k, n = 262144 + 77, 16384, 264
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(13)
+    x = torch.randn((m, k), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    x[-1, -1] = -80.0
+    torch.cuda.synchronize()
+    marks = [(1 << 31) // k, (1 << 32) // k]
+    rows = np.array(sorted({0, 1, 255, 256, m - 78, m - 77, m - 2, m - 1,
+                            *[r + d for r in marks for d in (-1, 0, 1)]}))
+    say("A past 4 GiB", m, k, n, "sampled rows", rows.tolist())
+    xs = host_bf16_bits(x[torch.from_numpy(rows).cuda()])
+    s_ref = oracle.scale_from_amax(np.float32(80.0))
+    aq_rows = oracle.quant_static(xs, s_ref)
+    a_q, s_a = fp8.quant_dynamic(x)
+    del x
+    w = synth.weights(11, n, k, row_multipliers=True)
+    b = synth.bias(11, n)
+    w_q, s_w = fp8.quant_weight(dev_bf16(w), True)
+    wq_ref, sw_ref = oracle.quant_weight(w, True)
+    torch.cuda.synchronize()
+    assert host_f32(s_a)[0] == s_ref
+    assert np.array_equal(host_u8(a_q[torch.from_numpy(rows).cuda()]), aq_rows)
+    assert np.array_equal(host_f32(s_w), sw_ref) and np.array_equal(host_u8(w_q), wq_ref)
+    ref = oracle.scaled_mm(aq_rows, wq_ref, s_ref, sw_ref, True, b)
+    for accum in ("fp32", "fp8"):
+        say("  accumulation", accum)
+        out = fp8.scaled_mm(a_q, w_q, s_a, s_w, True, dev_bf16(b), accum=accum)
+        torch.cuda.synchronize()
+        ob = host_bf16_bits(out[torch.from_numpy(rows).cuda()])
+        del out
+        assert_gemm_close(ob, ref, aq_rows, s_ref, wq_ref, sw_ref, True, bias_bits=b, accum=accum)
+
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("m,n", [(13, 130), (40, 72), (300, 520)])
 def test_longest_k_the_oracle_sums_exactly(m, n):
     """K = 131072, near the oracle's exactness limit (K < 171,196).  It

@@ -6,7 +6,7 @@ import torch
 import oracle
 import fp8_w8a8_quantized_amd as fp8
 from fp8_w8a8_quantized_amd import synth
-from _helpers import say, dev_bf16, host_u8, host_f32
+from _helpers import say, dev_bf16, host_u8, host_f32, host_bf16_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -202,3 +202,45 @@ def test_static_quant_prefill_size():
     q = fp8.quant_static(dev_bf16(x), s)
     torch.cuda.synchronize()
     assert np.array_equal(host_u8(q), oracle.quant_static(x, np.float32(0.05)))
+
+
+@pytest.mark.timeout(600)
+def test_quantizers_past_4_gib_sampled_rows():
+    """A bf16 tensor of 65536 x 32776 (4.3 GB, past 4 GiB): beyond the
+    buffer-load batches' 2 GiB range, so the dynamic (two launches),
+    static and per-row quantizers read it with 64-bit row addresses.  The
+    tensor is drawn on the device (N(0,1), far below 80 at this size) with
+    -80 planted in its last element, so the dynamic scale is fl32(80/448).
+    Rows on both sides of the 2 GiB and 4 GiB byte marks, and the first and
+    last rows, are compared with the oracle byte for byte; the per-row
+    scales of those rows too."""
+    rows, cols = 65536, 32776
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(12)
+    x = torch.randn((rows, cols), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    x[-1, -1] = -80.0
+    torch.cuda.synchronize()
+    row_bytes = cols * 2
+    marks = [(1 << 31) // row_bytes, (1 << 32) // row_bytes]
+    sample = sorted({0, 1, rows - 2, rows - 1, *[r + d for r in marks for d in (-1, 0, 1)]})
+    say("4 GiB tensor, sampled rows", sample)
+    xs = host_bf16_bits(x[sample])
+    s_ref = oracle.scale_from_amax(np.float32(80.0))
+
+    q, s = fp8.quant_dynamic(x)
+    torch.cuda.synchronize()
+    assert host_f32(s)[0] == s_ref
+    assert np.array_equal(host_u8(q[sample]), oracle.quant_static(xs, s_ref))
+    del q
+
+    s_static = torch.tensor([0.05], dtype=torch.float32, device="cuda")
+    q = fp8.quant_static(x, s_static)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u8(q[sample]), oracle.quant_static(xs, np.float32(0.05)))
+    del q
+
+    q, s_rows = fp8.quant_weight(x, True)
+    torch.cuda.synchronize()
+    q_ref, s_rows_ref = oracle.quant_weight(xs, True)
+    assert np.array_equal(host_f32(s_rows)[sample], s_rows_ref)
+    assert np.array_equal(host_u8(q[sample]), q_ref)
