@@ -129,3 +129,64 @@ def test_producers_at_prefill_size(which):
     s_ref = oracle.scale_from_amax(oracle.amax(oracle.bf16_bits_to_f32(y_ref)))
     assert host_f32(s)[0] == s_ref
     assert np.array_equal(host_u8(q)[rows], oracle.quant_static(y_ref[rows], s_ref))
+
+
+def _device_normal(shape, seed):
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    return torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+
+def _sample_rows(rows, row_bytes):
+    marks = [(1 << 31) // row_bytes, (1 << 32) // row_bytes]
+    return sorted({0, 1, rows - 2, rows - 1, *[r + d for r in marks for d in (-1, 0, 1) if 0 <= r + d < rows]})
+
+
+@pytest.mark.timeout(600)
+def test_producers_past_4_gib_sampled_rows():
+    """Both fused producers on inputs past 4 GiB, read with 64-bit row
+    addresses.  The inputs are drawn on the device (N(0,1)) with a planted
+    row that holds the tensor's largest value: for add + RMS norm, a last row
+    whose only nonzero entry normalizes to about sqrt(cols) = 181 (other rows
+    stay near 5); for SiLU*mul, gate = up = 80 in the last row (6400; other
+    products stay below about 40).  The oracle computes that row's values, so
+    it knows the scale, and compares the sampled rows' outputs and codes
+    byte for byte."""
+    rows, cols = 65536, 32776
+    h = _device_normal((rows, cols), 21)
+    d = _device_normal((rows, cols), 22)
+    h[-1].zero_(); d[-1].zero_()
+    h[-1, 5] = 100.0
+    torch.cuda.synchronize()
+    sample = _sample_rows(rows, cols * 2)
+    say("add_rmsnorm_quant past 4 GiB, sampled rows", sample)
+    idx = torch.tensor(sample, device="cuda")
+    h_rows, d_rows = host_bf16_bits(h[idx]), host_bf16_bits(d[idx])
+    h_out = torch.empty_like(h)
+    q, s, _, _ = fp8.add_rmsnorm_quant(h, d, h_out=h_out)
+    torch.cuda.synchronize()
+    del h, d
+    hs_ref = oracle.add_bf16(h_rows, d_rows)
+    y_ref = oracle.rmsnorm(hs_ref, 1e-5)
+    s_ref = oracle.scale_from_amax(np.max(np.abs(oracle.bf16_bits_to_f32(y_ref[-1]))))
+    assert host_f32(s)[0] == s_ref
+    assert np.array_equal(host_bf16_bits(h_out[idx]), hs_ref)
+    assert np.array_equal(host_u8(q[idx]), oracle.quant_static(y_ref, s_ref))
+    del h_out, q
+
+    rows, cols = 40000, 28680
+    gu = _device_normal((rows, 2 * cols), 23)
+    gu[-1, 3] = 80.0
+    gu[-1, cols + 3] = 80.0
+    torch.cuda.synchronize()
+    sample = _sample_rows(rows, 2 * cols * 2)
+    say("silu_mul_quant past 4 GiB, sampled rows", sample)
+    idx = torch.tensor(sample, device="cuda")
+    gu_rows = host_bf16_bits(gu[idx])
+    q, s, _ = fp8.silu_mul_quant(gu)
+    torch.cuda.synchronize()
+    del gu
+    y_ref = oracle.silu_mul(gu_rows, cols)
+    s_ref = oracle.scale_from_amax(np.max(np.abs(oracle.bf16_bits_to_f32(y_ref[-1]))))
+    assert host_f32(s)[0] == s_ref
+    assert np.array_equal(host_u8(q[idx]), oracle.quant_static(y_ref, s_ref))
