@@ -199,6 +199,44 @@ def test_activation_codes_past_4_gib_sampled_rows():
 
 
 @pytest.mark.timeout(600)
+@pytest.mark.parametrize("m,k,n", [(16, 16384, 270000), (16, 7936, 560000), (300, 16384, 270000)])
+def test_weights_past_4_gib_sampled_columns(m, k, n):
+    """W of 4.4 GB: the skinny kernel with interleaved K steps (K = 16384),
+    the two-block skinny kernel (K = 7936, under 32 steps of 256) and the
+    matrix-core kernel (M = 300) address weight rows past 2 and 4 GiB.  The
+    bf16 weights are drawn on the device (N(0, 0.02)); channelwise scales
+    depend on their own row only, so the oracle quantizes the sampled weight
+    rows itself (codes and scales must equal the GPU's) and checks the
+    output columns of those rows."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(14)
+    w = torch.randn((n, k), generator=gen, device="cuda", dtype=torch.bfloat16) * 0.02
+    torch.cuda.synchronize()
+    marks = [(1 << 31) // k, (1 << 32) // k]
+    cols = np.array(sorted({0, 1, n - 17, n - 2, n - 1, *[r + d for r in marks for d in (-1, 0, 1)]}))
+    say("W past 4 GiB", m, k, n, "sampled rows", cols.tolist())
+    idx = torch.from_numpy(cols).cuda()
+    w_rows = host_bf16_bits(w[idx])
+    w_q, s_w = fp8.quant_weight(w, True)
+    del w
+    wq_ref, sw_ref = oracle.quant_weight(w_rows, True)
+    x = synth.activations(12, m, k, outliers=True)
+    a_q, s_a = fp8.quant_dynamic(dev_bf16(x))
+    aq_ref, sa_ref = oracle.quant_dynamic(x)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_f32(s_w[idx]), sw_ref) and np.array_equal(host_u8(w_q[idx]), wq_ref)
+    assert host_f32(s_a)[0] == sa_ref and np.array_equal(host_u8(a_q), aq_ref)
+    ref = oracle.scaled_mm(aq_ref, wq_ref, sa_ref, sw_ref, True)
+    for accum in (("fp32", "fp8") if m > 64 else ("fp32",)):
+        say("  accumulation", accum)
+        out = fp8.scaled_mm(a_q, w_q, s_a, s_w, True, accum=accum)
+        torch.cuda.synchronize()
+        ob = host_bf16_bits(out[:, idx])
+        del out
+        assert_gemm_close(ob, ref, aq_ref, sa_ref, wq_ref, sw_ref, True, accum=accum)
+
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("m,n", [(13, 130), (40, 72), (300, 520)])
 def test_longest_k_the_oracle_sums_exactly(m, n):
     """K = 131072, near the oracle's exactness limit (K < 171,196).  It
