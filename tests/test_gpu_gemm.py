@@ -237,6 +237,29 @@ def test_weights_past_4_gib_sampled_columns(m, k, n):
 
 
 @pytest.mark.timeout(600)
+@pytest.mark.parametrize("k", [64, 24])
+def test_output_past_4_gib_sampled_rows(k):
+    """out = 65,549 x 32,776 bf16 (4.3 GB): the matrix-core kernel's tile
+    stores (K = 64) and the byte-granular skinny kernel's row stores (K = 24)
+    land past 2 and 4 GiB of the output.  Inputs come from the seeded
+    generators and are quantized on both sides (codes compared in full);
+    output rows around the 2 and 4 GiB marks, the first and the last rows
+    are checked."""
+    m, n = 65536 + 13, 32776
+    row_bytes = n * 2
+    marks = [(1 << 31) // row_bytes, (1 << 32) // row_bytes]
+    rows = np.array(sorted({0, 1, m - 14, m - 2, m - 1, *[r + d for r in marks for d in (-1, 0, 1)]}))
+    say("output past 4 GiB", m, k, n, "sampled rows", rows.tolist())
+    d = _prepare(13, m, k, n, per_channel=True, rowmul=True, with_bias=True)
+    out = fp8.scaled_mm(d["a_q"], d["w_q"], d["s_a"], d["s_w"], True, d["bias"])
+    torch.cuda.synchronize()
+    ob = host_bf16_bits(out[torch.from_numpy(rows).cuda()])
+    del out
+    ref = oracle.scaled_mm(d["aq"][rows], d["wq"], d["sa"], d["sw"], True, d["bias_bits"])
+    assert_gemm_close(ob, ref, d["aq"][rows], d["sa"], d["wq"], d["sw"], True, bias_bits=d["bias_bits"])
+
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("m,n", [(13, 130), (40, 72), (300, 520)])
 def test_longest_k_the_oracle_sums_exactly(m, n):
     """K = 131072, near the oracle's exactness limit (K < 171,196).  It
