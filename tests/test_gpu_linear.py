@@ -136,3 +136,43 @@ def test_linear_graph_replays():
         aq_ref, sa_ref = oracle.quant_dynamic(x)
         assert host_f32(s_a)[0] == sa_ref and np.array_equal(host_u8(a_q), aq_ref)
         assert np.array_equal(host_bf16_bits(out), host_bf16_bits(out2))
+
+
+def test_concurrent_streams_with_their_own_workspaces():
+    """Two streams run the whole linear back to back, eight calls each, with
+    their own workspace, operands and outputs: a 300 x 4096 -> 1030
+    activation (two-launch quantization, its per-block maxima in the
+    workspace) beside the 16 x 14336 -> 4096 decode input.  Each stream
+    also alternates between two inputs, so a stale maximum from another
+    call would change a scale.  Every output, code and scale equals the
+    same call made alone (and the oracle's codes and scale)."""
+    cases = [(300, 4096, 1030, 30), (16, 14336, 4096, 40)]
+    work = []
+    for m, k, n, cfg in cases:
+        d = _weights(cfg, m, k, n, True, rowmul=True, with_bias=True)
+        xs = [synth.activations(cfg + j, m, k, outliers=(j == 0), scale=[1.0, 5.0][j]) for j in range(2)]
+        xd = [dev_bf16(x) for x in xs]
+        refs = []
+        for j in range(2):
+            out, a_q, s_a = fp8.linear_dynamic(xd[j], d["w_q"], d["s_w"], True, d["bias"],
+                                               workspace=fp8.new_linear_workspace())
+            torch.cuda.synchronize()
+            aq_ref, sa_ref = oracle.quant_dynamic(xs[j])
+            assert host_f32(s_a)[0] == sa_ref and np.array_equal(host_u8(a_q), aq_ref)
+            refs.append((out.clone(), a_q.clone(), s_a.clone()))
+        work.append(dict(d=d, xd=xd, refs=refs, ws=fp8.new_linear_workspace(), stream=torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    results = [[] for _ in work]
+    for it in range(8):
+        for w, res in zip(work, results):
+            with torch.cuda.stream(w["stream"]):
+                out, a_q, s_a = fp8.linear_dynamic(w["xd"][it % 2], w["d"]["w_q"], w["d"]["s_w"], True,
+                                                   w["d"]["bias"], workspace=w["ws"])
+                res.append((it % 2, out, a_q, s_a))
+    torch.cuda.synchronize()
+    for (m, k, n, _), w, res in zip(cases, work, results):
+        say("concurrent stream", m, k, n, len(res), "calls")
+        for j, out, a_q, s_a in res:
+            ref_out, ref_q, ref_s = w["refs"][j]
+            assert torch.equal(s_a, ref_s) and torch.equal(a_q, ref_q)
+            assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
