@@ -4,7 +4,7 @@
 // decode runs at fewer than 16 rows, wants a dedicated GEMV-like kernel, and
 // must not pay for per-call packing or 16-padding.  Here the weight streams
 // from HBM straight into the matrix cores' A operand, one 16-row slice of W
-// per workgroup (two slices, up to 32 rows, for N of 16384 and more), each
+// per workgroup (two slices, up to 32 rows, for N of about 14300 and more), each
 // byte read once; the activation rows (at most 16) are the B operand, and
 // rows >= M are zeros in registers, never in memory.
 //
@@ -233,9 +233,6 @@ constexpr int kSkinnyDepth = 2;
 // Cache-policy bits of a buffer load (gfx950): nt, a non-temporal (streaming)
 // access.
 constexpr int kNonTemporal = 2;
-// Two weight blocks per wave once the halved grid still has 512 workgroups
-// (two per CU): below that the wider workgroups leave CUs idle.
-constexpr int kTwoBlockMinGrid = 512;
 
 // Compute units of the current device (looked up once per device).
 int device_cus() {
@@ -261,6 +258,14 @@ int two_block_rows(int64_t N) {
   const int64_t rows = (N + cus * per_cu - 1) / (cus * per_cu);
   return (int)std::min<int64_t>(32, (rows + 3) / 4 * 4);
 }
+
+// Two weight blocks per wave once N fills at least 7/4 x (CUs) workgroups of
+// 32 rows: N >= 14305 on 256 CUs.  Measured on per-tensor GEMMs at small M
+// with K = 4096 and the weights streaming from HBM: at N = 14336 (two
+// 28-row workgroups per CU instead of 3 or 4 one-block workgroups) 4-12%
+// faster for every M from 1 to 16; between N = 8192 and 14336 only M of 12
+// and more gained (3-7%), while M of 4 and less lost 1-3%.
+bool use_two_blocks(int64_t N) { return (N + 31) / 32 * 4 >= 7 * (int64_t)device_cus(); }
 
 template <int NW, int D, bool IL, bool NT, int FA, int FW>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(GemmArgs g) {
@@ -375,8 +380,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(GemmArgs g) {
   reduce_and_store(g, acc, red, NW, wave, lane, n0, m0, ep);
 }
 
-// Two 16-row weight blocks per wave, for N of 16384 and more with K below
-// 8192 (gate_up-sized layers).  Each activation step a wave loads serves
+// Two 16-row weight blocks per wave, for N of about 14300 and more with K
+// below 8192 (use_two_blocks).  Each activation step a wave loads serves
 // both blocks, so the texture path moves 1.5 lines per weight line instead
 // of 2.  Launched with one step in flight (112 VGPRs, four waves per SIMD):
 // on the 4096 -> 28672 decode shape, 23.3 -> 22.3 us against the one-block
@@ -743,7 +748,7 @@ hipError_t launch_skinny(const GemmArgs& g, hipStream_t stream) {
     const bool il = (g.K + 255) / 256 >= 32;
     const bool nt = (int64_t)g.N * g.K >= (int64_t(32) << 20);
     const dim3 block(kSkinnyWaves * 64);
-    if (!il && (g.N + 31) / 32 >= kTwoBlockMinGrid) {
+    if (!il && use_two_blocks(g.N)) {
       const int rw = two_block_rows(g.N);
       const dim3 grid2((unsigned)((g.N + rw - 1) / rw), (unsigned)tiles_m);
       if (nt)

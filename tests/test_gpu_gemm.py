@@ -56,11 +56,14 @@ def test_skinny_per_channel_llama_shapes(m, k, n):
 
 
 @pytest.mark.parametrize("m,k,n,pc", [(16, 4096, 16400, True), (3, 2048, 16392, False), (13, 1024, 16400, True),
-                                      (16, 4096, 28672, False), (9, 4096, 20000, True), (16, 1024, 30000, False)])
+                                      (16, 4096, 28672, False), (9, 4096, 20000, True), (16, 1024, 30000, False),
+                                      (11, 4096, 14305, True), (16, 4096, 14304, False)])
 def test_skinny_large_n_ragged(m, k, n, pc):
-    """N of 16384 and more with K below 8192 (two weight blocks per wave, 24,
-    28 or 32 rows per workgroup on 256 CUs): a last workgroup partly past N,
-    plain and non-temporal weight loads, per-tensor and channelwise."""
+    """N from the two-block threshold up (N >= 14305 on 256 CUs) with K below
+    8192: two weight blocks per wave, 24, 28 or 32 rows per workgroup, a last
+    workgroup partly past N (14305: 511 workgroups of 28 rows, the last with
+    25), plain and non-temporal weight loads, per-tensor and channelwise;
+    N = 14304, one below the threshold, takes the one-block kernel."""
     say("skinny large n", m, k, n, pc)
     d = _prepare(6, m, k, n, per_channel=pc, rowmul=pc, with_bias=pc)
     _run_and_check(d, pc)
