@@ -15,11 +15,13 @@ Workloads (synthetic, seeded; the models' shapes only -- no checkpoints):
   skinny   single per-tensor linears at small M: 16 x 4096 -> 4096, and
            Mistral-7B-shaped GEMMs at M in {1, 3, 7, 13} (and 32, 64) with
            N not a multiple of 16, weights rotated over >= 1 GiB per shape.
+  mid_m    the four Llama-3-8B GEMMs at M in {65, 128, 256}, between decode
+           and prefill.
 
 The default run (--workload all) prints the decode line (the headline value
 and roofline) with a "prefill" object (both accumulation modes, per shape)
-and a "skinny" object (per GEMM) added, so one line carries both halves of
-the metric.
+and "skinny", "mid_m" and "next" objects added, so one line carries both
+halves of the metric.
 
 Each step is captured once into a HIP graph and replayed (as a serving
 loop would); --eager launches every kernel from Python instead.
@@ -52,6 +54,7 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix throughput, published
 ROTATE_DECODE = 8
 ROTATE_MIN_BYTES = 1 << 30   # skinny GEMMs: weights rotated over at least this many bytes
 PREFILL_M = 16384
+MID_M = (65, 128, 256)
 
 
 def quant_bytes(m, k):
@@ -302,6 +305,42 @@ def bench_skinny(args):
             "mean_frac_hbm_m_le_16": round(float(np.mean([r["frac_hbm"] for r in hbm])), 4)}
 
 
+def bench_mid_m(args):
+    """GEMMs between decode and prefill: M in {65, 128, 256} rows on the
+    Llama-3-8B shapes (channelwise scales, fp32-class sums), each weight
+    rotated over copies totalling at least 1 GiB.  Up to 256 rows the call
+    gives problems too small for the matrix-core GEMM's 256 x 256 tiles to
+    the skinny kernel (weight read once per 64 rows of M).  A graph of one
+    launch per copy is timed; per GEMM: us, TFLOP/s, and GB/s of N*K + M*K +
+    2*M*N + 4*N + 4 bytes."""
+    log("building inputs: mid-M GEMMs")
+    rows = []
+    for sub, (name, k, n) in enumerate(synth.LLAMA3_8B_LINEARS):
+        w = synth.bf16_bits_to_torch(synth.weights(5, n, k, sub=sub, row_multipliers=True)).cuda()
+        w_q, s_w = fp8.quant_weight(w, per_channel=True)
+        del w
+        copies = [(w_q, s_w)] + [(w_q.clone(), s_w) for _ in range(-(-ROTATE_MIN_BYTES // (n * k)) - 1)]
+        torch.cuda.synchronize()
+        for m in MID_M:
+            x = synth.bf16_bits_to_torch(synth.activations(5, m, k, sub=3000 + m, outliers=True)).cuda()
+            a_q, s_a = fp8.quant_dynamic(x)
+            out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+
+            def launch(copies=copies, a_q=a_q, s_a=s_a, out=out):
+                for (wq, sw) in copies:
+                    fp8.scaled_mm(a_q, wq, s_a, sw, True, out=out)
+            t = time_eager_per_launch(launch, len(copies)) if args.eager else time_graph_per_launch(launch, len(copies))
+            b = gemm_bytes(m, k, n)
+            rows.append({"name": name, "M": m, "K": k, "N": n, "us": round(t * 1e6, 2),
+                         "TFLOPs": round(2 * m * n * k / t / 1e12, 1), "GBps": round(b / t / 1e9, 1),
+                         "rotation_copies": len(copies)})
+        del copies, w_q
+        torch.cuda.empty_cache()
+    return {"workload": "llama3-8b linears at M = 65, 128, 256 (between decode and prefill), channelwise weight "
+                        "scales, fp32-class sums, weights rotated over >= 1 GiB per shape",
+            "gemms": rows}
+
+
 def bench_next(args):
     """The calls beyond the headline path, each timed like the GEMMs (a graph
     of back-to-back calls, the median of five timed windows): the
@@ -546,10 +585,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", choices=["all", "decode", "prefill", "skinny", "chain", "next"], default="all",
+    ap.add_argument("--workload", choices=["all", "decode", "prefill", "skinny", "mid_m", "chain", "next"],
+                    default="all",
                     help="all (default): the decode line with prefill (both accumulation modes) and skinny "
                          "objects added; decode / prefill: that workload alone as the headline; skinny: the "
-                         "small-M per-tensor GEMMs alone; next: the producer-fused, static and weight "
+                         "small-M per-tensor GEMMs alone; mid_m: the GEMMs at M = 65, 128, 256 alone; next: the "
+                         "producer-fused, static and weight "
                          "quantizations and e5m2 GEMMs alone; chain: the 32-layer Llama-3-8B-shaped stack, "
                          "16 x 1024-token prefill, then decode steps at M=16 (--steps of them, default 512)")
     ap.add_argument("--accum", choices=["fp32", "fp8"], default="fp32",
@@ -575,6 +616,12 @@ def main():
         line = {"metric": METRIC + " -- calls beyond the headline path", "unit": "GB/s", "n_gpus": 1,
                 "higher_is_better": True, "data": "synthetic", "next": bench_next(args)}
         line["value"] = line["next"]["e5m2_decode_GBps"]
+        print(json.dumps(line), flush=True)
+        return
+    if args.workload == "mid_m":
+        line = {"metric": METRIC + " -- GEMMs between decode and prefill", "unit": "TFLOP/s", "n_gpus": 1,
+                "higher_is_better": True, "data": "synthetic", "mid_m": bench_mid_m(args)}
+        line["value"] = round(float(np.mean([r["TFLOPs"] for r in line["mid_m"]["gemms"]])), 1)
         print(json.dumps(line), flush=True)
         return
     if args.workload == "skinny":
@@ -649,6 +696,7 @@ def main():
         del lin
         torch.cuda.empty_cache()
         line["skinny"] = bench_skinny(args)
+        line["mid_m"] = bench_mid_m(args)
         line["next"] = bench_next(args)
     else:
         del lin

@@ -114,7 +114,8 @@ def _rel_l2(gpu_bits, ref_bits):
 @pytest.mark.parametrize("m", [16, 96])
 def test_stack_against_an_oracle_run_of_the_whole_stack(stack, oracle_weights, m):
     """The GPU stack against the oracle's own run of it (M = 16: the skinny
-    GEMMs; M = 96: the matrix-core GEMM on the pitched code slices).
+    GEMMs; M = 96: the skinny kernel in two grid rows of M for QKV, O and
+    down, and the matrix-core GEMM for gate_up, on the pitched code slices).
 
     Nothing of the GPU's enters the oracle's run, so the two drift apart
     where rounding differs.  With the same codes on both sides an output

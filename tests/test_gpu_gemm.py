@@ -101,15 +101,42 @@ def test_mid_m(m, k, n):
     _run_and_check(d, False)
 
 
-# ------------------------------------------------------ matrix-core GEMM (M > 64)
+# ------------------------------ matrix-core GEMM (M > 64 with enough output tiles)
 @pytest.mark.parametrize("accum", ["fp32", "fp8"])
 @pytest.mark.parametrize("m,k,n,pc", [
-    (256, 256, 256, False), (512, 4096, 1024, True), (300, 4096, 4100, False),
-    (777, 1040, 520, True), (65, 128, 16, False), (1000, 4096, 6144, True)])
+    (256, 256, 12288, False), (512, 4096, 1024, True), (300, 4096, 4100, False),
+    (777, 1040, 520, True), (65, 128, 24576, False), (1000, 4096, 6144, True)])
 def test_mfma_gemm(m, k, n, pc, accum):
+    """The matrix-core GEMM: M > 256, or M of 65 and 256 with N large enough
+    that the call does not give the problem to the skinny kernel (one row of
+    tiles, mostly past M for M = 65)."""
     say("mfma", m, k, n, pc, accum)
     d = _prepare(3, m, k, n, per_channel=pc, outliers=pc, rowmul=pc, with_bias=(m % 2 == 0))
     _run_and_check(d, pc, accum=accum)
+
+
+@pytest.mark.parametrize("accum", ["fp32", "fp8"])
+@pytest.mark.parametrize("m,k,n", [(65, 4096, 1030), (128, 4096, 4096), (256, 256, 256), (200, 14336, 300),
+                                   (96, 4096, 14336), (256, 4096, 6144)])
+def test_mid_m_problems_too_small_for_the_matrix_core_tiles(m, k, n, accum):
+    """64 < M <= 256 with N * ceil(M / 64) below the matrix-core GEMM's
+    threshold (49152 for fp32-class sums, 32768 for fp8 sums): the skinny
+    kernel runs, in grid rows of 64 rows of M, and sums with fp32-class
+    precision whatever the mode asked for, so both modes meet the fp32
+    bound and give the same bits.  (96 x 4096 -> 14336 crosses over: the
+    skinny kernel with fp32 sums, the matrix-core GEMM with fp8 sums.)"""
+    say("mid m", m, k, n, accum)
+    d = _prepare(7, m, k, n, per_channel=True, outliers=True, rowmul=True, with_bias=True)
+    skinny = n * ((m + 63) // 64) < (32768 if accum == "fp8" else 49152)
+    out = fp8.scaled_mm(d["a_q"], d["w_q"], d["s_a"], d["s_w"], True, d["bias"], accum=accum)
+    torch.cuda.synchronize()
+    ref = oracle.scaled_mm(d["aq"], d["wq"], d["sa"], d["sw"], True, d["bias_bits"])
+    assert_gemm_close(host_bf16_bits(out), ref, d["aq"], d["sa"], d["wq"], d["sw"], True, bias_bits=d["bias_bits"],
+                      accum="fp32" if skinny else accum)
+    if skinny and accum == "fp8":
+        exact = fp8.scaled_mm(d["a_q"], d["w_q"], d["s_a"], d["s_w"], True, d["bias"], accum="fp32")
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), exact.view(torch.int16))
 
 
 @pytest.mark.parametrize("accum", ["fp32", "fp8"])

@@ -57,13 +57,15 @@ def test_linear_decode_shapes(m, k, n, pc, bias):
     _check(x, dev_bf16(x), d, pc, ws)
 
 
-# M above 64 (matrix-core GEMM), a large activation, a misaligned activation
-# view (element-wise loads), K % 16 != 0 (byte-granular skinny kernel)
-@pytest.mark.parametrize("case", ["m65", "big_act", "x_view", "k_ragged"])
+# M above 64 on a problem too small for the matrix-core tiles (skinny kernel,
+# two grid rows) and above 256 (matrix-core GEMM), a large activation, a
+# misaligned activation view (element-wise loads), K % 16 != 0 (byte-granular
+# skinny kernel)
+@pytest.mark.parametrize("case", ["m65", "m300", "big_act", "x_view", "k_ragged"])
 def test_linear_other_shapes(case):
     say("linear other", case)
-    m, k, n = {"m65": (65, 1024, 520), "big_act": (64, 32784, 64), "x_view": (16, 4096, 1030),
-               "k_ragged": (9, 4100, 33)}[case]
+    m, k, n = {"m65": (65, 1024, 520), "m300": (300, 1024, 520), "big_act": (64, 32784, 64),
+               "x_view": (16, 4096, 1030), "k_ragged": (9, 4100, 33)}[case]
     x = synth.activations(4, m, k + (1 if case == "x_view" else 0))
     xd = dev_bf16(x)
     if case == "x_view":

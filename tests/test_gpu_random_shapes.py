@@ -6,7 +6,9 @@ fixed seed. Together the cases cross every dispatch path of the library:
 - the one- and two-block skinny kernels (M <= 16);
 - the multi-block skinny kernel (16 < M <= 64);
 - the byte-granular kernel (K % 16 != 0 or unaligned pitches);
-- the matrix-core kernel (M > 64), with vector and 2-byte output stores.
+- the matrix-core kernel (M > 64 with enough output tiles), with vector and
+  2-byte output stores, and the multi-block skinny kernel for the 64 < M <= 256
+  problems too small for its tiles.
 The operands are quantized from the seeded generators on each side
 independently, and the GPU's codes must equal the oracle's byte for byte.
 """
