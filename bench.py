@@ -15,8 +15,8 @@ Workloads (synthetic, seeded; the models' shapes only -- no checkpoints):
   skinny   single per-tensor linears at small M: 16 x 4096 -> 4096, and
            Mistral-7B-shaped GEMMs at M in {1, 3, 7, 13} (and 32, 64) with
            N not a multiple of 16, weights rotated over >= 1 GiB per shape.
-  mid_m    the four Llama-3-8B GEMMs at M in {65, 128, 256}, between decode
-           and prefill.
+  mid_m    the four Llama-3-8B GEMMs at M in {65, 128, 256, 512, 1024},
+           between decode and prefill.
 
 The default run (--workload all) prints the decode line (the headline value
 and roofline) with a "prefill" object (both accumulation modes, per shape)
@@ -54,7 +54,7 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix throughput, published
 ROTATE_DECODE = 8
 ROTATE_MIN_BYTES = 1 << 30   # skinny GEMMs: weights rotated over at least this many bytes
 PREFILL_M = 16384
-MID_M = (65, 128, 256)
+MID_M = (65, 128, 256, 512, 1024)
 
 
 def quant_bytes(m, k):
@@ -237,7 +237,7 @@ def bench_prefill_modes(weights_from, args):
         step_ms = time_steps(lin, ws, accum, steps=args.prefill_steps, warmup=2)
         per = gemm_times(lin, accum, reps=3)
         gemm_tflops = sum(flops) / sum(per) / 1e12
-        r = {"kernel": f"gemm_mfma_kernel<{'true' if accum == 'fp32' else 'false'}, true, 0, 0>",
+        r = {"kernel": f"gemm_mfma_kernel<4, {'true' if accum == 'fp32' else 'false'}, true, 0, 0>",
              "sums": ("bf16 matrix cores on exactly converted e4m3 values (fp32-class sums; the default)"
                       if accum == "fp32" else "fp8 matrix cores (13-bit sums inside each group of 8 products)"),
              "per_shape_us": {L["name"]: round(t * 1e6, 2) for L, t in zip(lin, per)},
@@ -306,11 +306,11 @@ def bench_skinny(args):
 
 
 def bench_mid_m(args):
-    """GEMMs between decode and prefill: M in {65, 128, 256} rows on the
-    Llama-3-8B shapes (channelwise scales, fp32-class sums), each weight
-    rotated over copies totalling at least 1 GiB.  Up to 256 rows the call
-    gives problems too small for the matrix-core GEMM's 256 x 256 tiles to
-    the skinny kernel (weight read once per 64 rows of M).  A graph of one
+    """GEMMs between decode and prefill: M in {65, 128, 256, 512, 1024} rows
+    on the Llama-3-8B shapes (channelwise scales, fp32-class sums), each
+    weight rotated over copies totalling at least 1 GiB.  The call gives
+    problems too small for the matrix-core tiles to the skinny kernel and
+    runs 128 x 128 tiles where 256 x 256 ones are too few.  A graph of one
     launch per copy is timed; per GEMM: us, TFLOP/s, and GB/s of N*K + M*K +
     2*M*N + 4*N + 4 bytes."""
     log("building inputs: mid-M GEMMs")
@@ -336,7 +336,7 @@ def bench_mid_m(args):
                          "rotation_copies": len(copies)})
         del copies, w_q
         torch.cuda.empty_cache()
-    return {"workload": "llama3-8b linears at M = 65, 128, 256 (between decode and prefill), channelwise weight "
+    return {"workload": "llama3-8b linears at M = 65, 128, 256, 512, 1024 (between decode and prefill), channelwise weight "
                         "scales, fp32-class sums, weights rotated over >= 1 GiB per shape",
             "gemms": rows}
 
@@ -589,7 +589,7 @@ def main():
                     default="all",
                     help="all (default): the decode line with prefill (both accumulation modes) and skinny "
                          "objects added; decode / prefill: that workload alone as the headline; skinny: the "
-                         "small-M per-tensor GEMMs alone; mid_m: the GEMMs at M = 65, 128, 256 alone; next: the "
+                         "small-M per-tensor GEMMs alone; mid_m: the GEMMs at M = 65 to 1024 alone; next: the "
                          "producer-fused, static and weight "
                          "quantizations and e5m2 GEMMs alone; chain: the 32-layer Llama-3-8B-shaped stack, "
                          "16 x 1024-token prefill, then decode steps at M=16 (--steps of them, default 512)")
@@ -672,7 +672,7 @@ def main():
         value = step_flops / (ms_per_step * 1e-3) / 1e12
         unit = "TFLOP/s"
         achieved = per_launch_flops / avg_launch_s / 1e12
-        kernel = f"gemm_mfma_kernel<{'false' if args.accum == 'fp8' else 'true'}, true, 0, 0>"
+        kernel = f"gemm_mfma_kernel<4, {'false' if args.accum == 'fp8' else 'true'}, true, 0, 0>"
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": recorded_traffic(kernel),
                 "kernel": kernel, "avg_launch_us": round(avg_launch_s * 1e6, 2),

@@ -49,20 +49,19 @@ fp8_status check_fmt(const char* fn, fp8_format f) {
   return FP8_OK;
 }
 
-// Up to 256 rows the matrix-core GEMM has ceil(N / 256) tiles of 256 x 256
-// (one per CU at a time), too few to occupy the GPU unless N is large; its
-// time is then about one tile's, proportional to K whatever M.  The skinny
-// kernel reads the weight once per 64 rows of M instead, a time
-// proportional to N K ceil(M / 64).  Measured with the weights streaming
-// from HBM (K = 4096 and 14336, N = 4096 to 14336): the skinny kernel is
-// the faster while N ceil(M / 64) < 49152 with fp32-class sums (65 x 4096
-// -> 4096: 15 against 80 us; 256 x 14336 -> 4096: 110 against 265 us; but
-// 256 x 4096 -> 14336: 105 against 85 us), and while it is < 32768 with the
-// fp8 matrix cores' sums, whose tiles take about 0.6 of that time.  The
-// skinny kernel always sums with fp32-class precision.
-bool few_tiles_for_matrix_cores(int64_t M, int64_t N, bool fp8_sums) {
-  return M <= 256 && N * ((M + 63) / 64) < (fp8_sums ? 32768 : 49152);
-}
+// Up to 256 rows the matrix-core GEMM has at most 2 ceil(N / 128) tiles of
+// 128 x 128 (one per CU at a time), so for N up to some 16k it runs a single
+// round of tiles whose time is proportional to K whatever M and N: about 36
+// us at K = 4096 with fp32-class sums, 29-31 us with fp8 sums.  The skinny
+// kernel reads the weight once per 64 rows of M instead, about 1.75 us per
+// 1024 of N ceil(M / 64) at K = 4096.  So the skinny kernel runs while
+// N ceil(M / 64) < 20480 (in both modes: 256 x 4096 -> 4096 took 28 us on
+// it against 31 us on the fp8 matrix cores).  Measured, 65-128 x 4096 ->
+// 4096 in 15-17 us and 65-128 x 14336 -> 4096 in 49-55 us on it, while
+// 65-128 x 4096 -> 14336 takes 49-52 us on it and 38-39 us on the
+// matrix-core GEMM.  The skinny kernel always sums with fp32-class
+// precision.
+bool few_tiles_for_matrix_cores(int64_t M, int64_t N) { return M <= 256 && N * ((M + 63) / 64) < 20480; }
 
 // ---- scratch of the no-allocation entry point ----------------------------
 // The dynamic quantization's per-block maxima (quant_workspace_bytes(), the
@@ -274,7 +273,7 @@ fp8_status fp8_scaled_mm_fmt(const uint8_t* a_q, int64_t lda, fp8_format fmt_a, 
 
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
   const bool fp8_sums = accum == FP8_ACCUM_FP8_MFMA;
-  if (M > 64 && !few_tiles_for_matrix_cores(M, N, fp8_sums) && tiles < (1ll << 31) &&
+  if (M > 64 && !few_tiles_for_matrix_cores(M, N) && tiles < (1ll << 31) &&
       fp8w8a8::gemm_mfma_supported(g))
     return hip_status(fp8w8a8::launch_gemm_mfma(g, fp8_sums, s), fn);
 

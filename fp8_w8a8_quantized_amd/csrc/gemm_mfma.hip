@@ -10,7 +10,11 @@
 // Design for CDNA4:
 //   * 256 x 256 output tile, 128 k per step; 4 waves, each owning a
 //     128 x 128 quarter as 4 x 4 blocks of 32 x 32 matrix-core products
-//     (256 fp32 accumulators per lane).
+//     (256 fp32 accumulators per lane).  Where such tiles are too few to
+//     occupy the GPU (M of a few hundred to a few thousand rows), the same
+//     kernel runs 128 x 128 tiles: 2 x 2 blocks per wave, 64 accumulators,
+//     everything below scaled to the tile (template WB, blocks per wave
+//     and dimension).
 //   * Both operands are K-contiguous ([M, K] and [N, K]), the matrix cores'
 //     native operand layout: every lane reads 32 contiguous k-bytes of one
 //     row, so no transposition is needed anywhere.
@@ -67,6 +71,7 @@
 //     v_mfma_f32_32x32x16_bf16, whose sums keep fp32-class precision; the
 //     LDS tiles, the loads and the HBM traffic are the same in both modes.
 
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -78,18 +83,30 @@ namespace {
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int BK = 128;
 constexpr int kThreads = 256;
-constexpr int kOperandBytes = BM * BK;  // 32 KiB per operand per stage
-constexpr int kStageBytes = 2 * kOperandBytes;
 constexpr int kGroupM = 8;
-// per-tile epilogue parameters: 256 column scales (fp32) and biases (bf16)
-constexpr int kEpiParamBytes = BN * 4 + BN * 2;
 // L2 prefetch: two 4-byte-per-lane DMA loads per wave and step, landing in a
 // junk LDS area nobody reads (512 bytes per wave)
 constexpr int kPrefetchBytes = 4 * 512;
-constexpr int kLdsBytes = 2 * kStageBytes + 2 * kEpiParamBytes + kPrefetchBytes;
-static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+
+// Tile geometry.  WB = 32 x 32 product blocks per wave in each dimension;
+// the 4 waves of a workgroup form a 2 x 2 grid, so a tile is TILE x TILE
+// with TILE = 64 WB: 256 (WB = 4), or 128 (WB = 2) for problems whose
+// 256 x 256 tiles are too few to occupy the GPU.
+template <int WB>
+struct Geo {
+  static constexpr int TILE = 64 * WB;
+  static constexpr int kOperandBytes = TILE * BK;  // per operand per stage (32 KiB at TILE 256)
+  static constexpr int kStageBytes = 2 * kOperandBytes;
+  // per-tile epilogue parameters: TILE column scales (fp32) and biases (bf16)
+  static constexpr int kEpiParamBytes = TILE * 4 + TILE * 2;
+  static constexpr int kLdsBytes = 2 * kStageBytes + 2 * kEpiParamBytes + kPrefetchBytes;
+  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+  // 8-row (1 KiB) DMA blocks each wave loads per operand and step
+  static constexpr int NB = TILE / 32;
+  static constexpr int kStepLoads = 2 * NB;  // DMA instructions per wave and step
+};
 // vector-memory instructions a wave issues besides the operand loads: the L2
 // prefetch after each step's loads (fp8 mode) and the two parameter loads at
 // a tile's first step
@@ -97,7 +114,6 @@ constexpr int kPrefetchOps = 2;
 // how many steps the L2 prefetch runs ahead of the DMA loads
 constexpr int kPrefetchAhead = 1;
 constexpr int kParamOps = 2;
-constexpr int kStepLoads = 16;  // DMA instructions per wave and step (8 blocks x 2 operands)
 
 // XOR swizzle of the 16-byte chunks of a 128-byte LDS row.  The 16 rows a
 // half-wave reads at one logical chunk land on 16 distinct (bank-pair,
@@ -139,7 +155,9 @@ struct Tile {
   __amdgpu_buffer_rsrc_t ra, rw, ro;
 };
 
+template <int TILE>
 __device__ __forceinline__ Tile tile_at(const GemmArgs& g, int b, int tiles_m, int tiles_n) {
+  constexpr int BM = TILE, BN = TILE;
   const int T = tiles_m * tiles_n;
   if ((T & 7) == 0) b = (b & 7) * (T >> 3) + (b >> 3);
   const int per_group = kGroupM * tiles_n;
@@ -166,9 +184,13 @@ __device__ __forceinline__ Tile tile_at(const GemmArgs& g, int b, int tiles_m, i
 
 // VEC: N % 8 == 0, ldo % 8 == 0 and a 16-byte aligned output, so every lane
 // writes whole 16-byte chunks (a fixed count of stores per tile).
-template <bool EXACT, bool VEC, int FA, int FW>
+template <int WB, bool EXACT, bool VEC, int FA, int FW>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
+  using G = Geo<WB>;
+  constexpr int TILE = G::TILE, HALF = TILE / 2, NB = G::NB;
+  constexpr int kOperandBytes = G::kOperandBytes, kStageBytes = G::kStageBytes;
+  constexpr int kEpiParamBytes = G::kEpiParamBytes, kStepLoads = G::kStepLoads;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[G::kLdsBytes];
   uint8_t* const params = smem + 2 * kStageBytes;  // two parameter buffers, by tile parity
   uint8_t* const pf_junk = params + 2 * kEpiParamBytes;
 
@@ -186,11 +208,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
   // which global chunk each lane fetches.  Block b of an operand is loaded
   // by wave b / 8.  Lanes whose chunk lies past K, and whole steps past the
   // last tile, load zeros (out-of-range offset).
-  uint32_t dvoff_a[8], dvoff_w[8];
+  uint32_t dvoff_a[NB], dvoff_w[NB];
   const int drow_in_blk = lane >> 3, dphys = lane & 7;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = (wave * 8 + i) * 8 + drow_in_blk;
+  for (int i = 0; i < NB; ++i) {
+    const int row = (wave * NB + i) * 8 + drow_in_blk;
     const int c = dphys ^ swz(row);
     dvoff_a[i] = (uint32_t)(row * g.lda + c * 16);
     dvoff_w[i] = (uint32_t)(row * g.ldw + c * 16);
@@ -203,12 +225,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
   // two steps ahead of the products, across tile boundaries; past the last
   // tile its loads fetch zeros.
   int lb = blockIdx.x, lkt = 0;
-  Tile lt = tile_at(g, lb, tiles_m, tiles_n);
+  Tile lt = tile_at<TILE>(g, lb, tiles_m, tiles_n);
   auto advance_load = [&]() {
     if (++lkt == KT) {
       lkt = 0;
       lb += gridDim.x;
-      if (lb < T) lt = tile_at(g, lb, tiles_m, tiles_n);
+      if (lb < T) lt = tile_at<TILE>(g, lb, tiles_m, tiles_n);
     }
   };
   // one block of each operand of the load cursor's step (2 instructions)
@@ -217,7 +239,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
     const bool kin = lb < T && k0 + ((i & 1) ? dchunk_k1 : dchunk_k0) < g.K;
     uint8_t* As = smem + stage * kStageBytes;
     uint8_t* Ws = As + kOperandBytes;
-    const int blk = __builtin_amdgcn_readfirstlane(wave * 8 + i);
+    const int blk = __builtin_amdgcn_readfirstlane(wave * NB + i);
     const uint32_t oa = kin ? dvoff_a[i] + k0 : kOutOfRange;
     const uint32_t ow = kin ? dvoff_w[i] + k0 : kOutOfRange;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(lt.ra, (__attribute__((address_space(3))) void*)(As + blk * 1024), 16,
@@ -232,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
     if (++pkt == KT) {
       pkt = 0;
       pb += gridDim.x;
-      if (pb < T) pt = tile_at(g, pb, tiles_m, tiles_n);
+      if (pb < T) pt = tile_at<TILE>(g, pb, tiles_m, tiles_n);
     }
   };
   // L2 prefetch of the prefetch cursor's step, which then advances.
@@ -244,13 +266,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
   // junk LDS area (no registers to hold, nothing waits on them); for other
   // tile layouts they merely touch lines of this tile's own panels.
   auto prefetch = [&]() {
-    const int tm = pt.m0 / BM, tn = pt.n0 / BN;
+    const int tm = pt.m0 / TILE, tn = pt.n0 / TILE;
     const bool valid = pb < T;
     const int s = pkt * BK;
     const uint32_t oa =
-        (valid && lane < 16) ? (uint32_t)((64 * (tn & 3) + 16 * wave + lane) * g.lda + s) : kOutOfRange;
+        (valid && lane < TILE / 16) ? (uint32_t)(((TILE / 4) * (tn & 3) + (TILE / 16) * wave + lane) * g.lda + s)
+                                    : kOutOfRange;
     const uint32_t ow =
-        (valid && lane < 8) ? (uint32_t)((32 * (tm & 7) + 8 * wave + lane) * g.ldw + s) : kOutOfRange;
+        (valid && lane < TILE / 32) ? (uint32_t)(((TILE / 8) * (tm & 7) + (TILE / 32) * wave + lane) * g.ldw + s)
+                                    : kOutOfRange;
     uint8_t* J = pf_junk + __builtin_amdgcn_readfirstlane(wave * 512);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(pt.ra, (__attribute__((address_space(3))) void*)J, 4, (int)oa, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(pt.rw, (__attribute__((address_space(3))) void*)(J + 256), 4, (int)ow, 0,
@@ -277,28 +301,34 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
   // never stored.
   auto load_params = [&](const Tile& t, uint8_t* P) {
     float* Psc = reinterpret_cast<float*>(P);
-    uint16_t* Pbias = reinterpret_cast<uint16_t*>(P + BN * 4);
+    uint16_t* Pbias = reinterpret_cast<uint16_t*>(P + TILE * 4);
+    // waves past the tile's columns (TILE 128: waves 2 and 3 for the scales,
+    // 1 to 3 for the biases) load nothing into the junk area
+    const bool sc_wave = TILE >= 4 * 64 || wave < TILE / 64;
     const int nc = t.n0 + wave * 64 + lane;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rsw, (__attribute__((address_space(3))) void*)(Psc + __builtin_amdgcn_readfirstlane(wave * 64)), 4,
-        (int)(g.per_channel ? (nc < g.N ? (uint32_t)nc * 4 : kOutOfRange) : 0u), 0, 0, 0);
+        rsw,
+        (__attribute__((address_space(3))) void*)(sc_wave ? Psc + __builtin_amdgcn_readfirstlane(wave * 64)
+                                                          : reinterpret_cast<float*>(pf_junk)),
+        4, (int)(!sc_wave ? kOutOfRange : g.per_channel ? (nc < g.N ? (uint32_t)nc * 4 : kOutOfRange) : 0u), 0, 0, 0);
     // VEC: N % 8 == 0, so no dword of two biases straddles the end
     const int nb2 = t.n0 + (wave & 1) * 128 + 2 * lane;
-    const bool bias_ok = VEC && wave < 2 && nb2 < g.N;
+    const bool bias_ok = VEC && wave < TILE / 128 && nb2 < g.N;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rbias,
-        (__attribute__((address_space(3))) void*)(wave < 2 ? Pbias + __builtin_amdgcn_readfirstlane(wave * 128)
-                                                             : reinterpret_cast<uint16_t*>(pf_junk)),
+        (__attribute__((address_space(3))) void*)(wave < TILE / 128
+                                                      ? Pbias + __builtin_amdgcn_readfirstlane(wave * 128)
+                                                      : reinterpret_cast<uint16_t*>(pf_junk)),
         4, (int)(bias_ok ? (uint32_t)nb2 * 2 : kOutOfRange), 0, 0, 0);
   };
 
   // ---- prologue: the first two steps' loads, then the first step's
   // first-half fragments
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dma_part(0, i);
+  for (int i = 0; i < NB; ++i) dma_part(0, i);
   advance_load();
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dma_part(1, i);
+  for (int i = 0; i < NB; ++i) dma_part(1, i);
   advance_load();
   advance_prefetch();
   advance_prefetch();
@@ -308,15 +338,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
   }
   __builtin_amdgcn_s_waitcnt(wait_vmcnt(kStepLoads + kPf * kPrefetchAhead));
   __builtin_amdgcn_s_barrier();
-  v8i wf0[4], af0[4], wf1[4], af1[4];
+  v8i wf0[WB], af0[WB], wf1[WB], af1[WB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) wf0[i] = read_frag(smem + kOperandBytes, wn * 128 + i * 32 + frow, fchunk);
+  for (int i = 0; i < WB; ++i) wf0[i] = read_frag(smem + kOperandBytes, wn * HALF + i * 32 + frow, fchunk);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) af0[j] = read_frag(smem, wm * 128 + j * 32 + frow, fchunk);
+  for (int j = 0; j < WB; ++j) af0[j] = read_frag(smem, wm * HALF + j * 32 + frow, fchunk);
 
   int step = 0;   // steps done over all tiles: stage parity
   int tcount = 0;  // tiles done: parameter-buffer parity
-  v16f acc[4][4];
+  v16f acc[WB][WB];
+  // product pairs per half step (fp8 mode), and per pair: fragment reads and
+  // DMA parts (one of each at WB = 4)
+  constexpr int NP = WB * WB / 2, RPP = 2 * WB / NP, DPP = NB / NP;
+  // exact mode: DMA parts per 16-deep slice
+  constexpr int DPT = NB / 4;
   // One k step (see the design notes above).  FIRST: the tile's first step
   // (its parameter loads).  LAST: the tile's last step, whose second half
   // issues no loads and reads no fragments: its stage becomes the
@@ -336,32 +371,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
     // ---- first half: its products, with the second half's fragment reads
     if constexpr (!EXACT) {
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
+      for (int p = 0; p < NP; ++p) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const int i = (2 * p + q) >> 2, j = (2 * p + q) & 3;
+          const int i = (2 * p + q) / WB, j = (2 * p + q) % WB;
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf0[i], af0[j], acc[i][j], FW, FA, 0, 0, 0,
                                                                        0);
         }
-        if (p < 4) wf1[p] = read_frag(Ws, wn * 128 + p * 32 + frow, 4 + fchunk);
-        else af1[p - 4] = read_frag(As, wm * 128 + (p - 4) * 32 + frow, 4 + fchunk);
+#pragma unroll
+        for (int r = p * RPP; r < (p + 1) * RPP; ++r) {
+          if (r < WB) wf1[r] = read_frag(Ws, wn * HALF + r * 32 + frow, 4 + fchunk);
+          else af1[r - WB] = read_frag(As, wm * HALF + (r - WB) * 32 + frow, 4 + fchunk);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        bf16x8 wb[4], ab[4];
+        bf16x8 wb[WB], ab[WB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wb[i] = slice_bf16<FW>(wf0[i], t);
+        for (int i = 0; i < WB; ++i) wb[i] = slice_bf16<FW>(wf0[i], t);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ab[j] = slice_bf16<FA>(af0[j], t);
+        for (int j = 0; j < WB; ++j) ab[j] = slice_bf16<FA>(af0[j], t);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < WB; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < WB; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb[i], ab[j], acc[i][j], 0, 0, 0);
-        wf1[t] = read_frag(Ws, wn * 128 + t * 32 + frow, 4 + fchunk);
-        af1[t] = read_frag(As, wm * 128 + t * 32 + frow, 4 + fchunk);
+        if (t < WB) {
+          wf1[t] = read_frag(Ws, wn * HALF + t * 32 + frow, 4 + fchunk);
+          af1[t] = read_frag(As, wm * HALF + t * 32 + frow, 4 + fchunk);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -383,43 +423,49 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
     // first-half fragment reads
     if constexpr (!EXACT) {
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
+      for (int p = 0; p < NP; ++p) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const int i = (2 * p + q) >> 2, j = (2 * p + q) & 3;
+          const int i = (2 * p + q) / WB, j = (2 * p + q) % WB;
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf1[i], af1[j], acc[i][j], FW, FA, 0, 0, 0,
                                                                        0);
         }
         if constexpr (!LAST) {
-          dma_part(step & 1, p);
-          if (p == 7) {
+#pragma unroll
+          for (int d = p * DPP; d < (p + 1) * DPP; ++d) dma_part(step & 1, d);
+          if (p == NP - 1) {
             advance_load();
             prefetch();
           }
-          if (p < 4) wf0[p] = read_frag(Wn, wn * 128 + p * 32 + frow, fchunk);
-          else af0[p - 4] = read_frag(An, wm * 128 + (p - 4) * 32 + frow, fchunk);
+#pragma unroll
+          for (int r = p * RPP; r < (p + 1) * RPP; ++r) {
+            if (r < WB) wf0[r] = read_frag(Wn, wn * HALF + r * 32 + frow, fchunk);
+            else af0[r - WB] = read_frag(An, wm * HALF + (r - WB) * 32 + frow, fchunk);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        bf16x8 wb[4], ab[4];
+        bf16x8 wb[WB], ab[WB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wb[i] = slice_bf16<FW>(wf1[i], t);
+        for (int i = 0; i < WB; ++i) wb[i] = slice_bf16<FW>(wf1[i], t);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ab[j] = slice_bf16<FA>(af1[j], t);
+        for (int j = 0; j < WB; ++j) ab[j] = slice_bf16<FA>(af1[j], t);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < WB; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < WB; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb[i], ab[j], acc[i][j], 0, 0, 0);
         if constexpr (!LAST) {
-          dma_part(step & 1, 2 * t);
-          dma_part(step & 1, 2 * t + 1);
+#pragma unroll
+          for (int d = t * DPT; d < (t + 1) * DPT; ++d) dma_part(step & 1, d);
           if (t == 3) advance_load();
-          wf0[t] = read_frag(Wn, wn * 128 + t * 32 + frow, fchunk);
-          af0[t] = read_frag(An, wm * 128 + t * 32 + frow, fchunk);
+          if (t < WB) {
+            wf0[t] = read_frag(Wn, wn * HALF + t * 32 + frow, fchunk);
+            af0[t] = read_frag(An, wm * HALF + t * 32 + frow, fchunk);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -430,12 +476,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
   using False = std::integral_constant<bool, false>;
 
   for (int b = blockIdx.x; b < T; b += gridDim.x, ++tcount) {
-    const Tile cur = tile_at(g, b, tiles_m, tiles_n);
+    const Tile cur = tile_at<TILE>(g, b, tiles_m, tiles_n);
     uint8_t* const P = params + (tcount & 1) * kEpiParamBytes;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WB; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < WB; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
     if (KT == 1) {
@@ -449,11 +495,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
     // ---- epilogue.  acc[i][j] = D[n][m] for the 32x32 block (i: n, j: m):
     // lane holds m = lane % 32 and, in registers 4q..4q+3, the four
     // consecutive columns n = 8q + 4 * (lane / 32) + 0..3.  Each round parks
-    // the 32 rows of block-row j (fp32, 512-byte LDS rows, 16-byte chunk c of
-    // row r at c ^ r) in the last step's stage -- rows 0..15 in the 8 KiB of
-    // its A part and rows 16..31 in the 8 KiB of its W part that this wave's
-    // own loads fill, so no other wave touches them -- and reads them back
-    // as 8 consecutive columns per lane.
+    // the 32 rows of block-row j (fp32, HALF columns: LDS rows of 4 HALF
+    // bytes, 16-byte chunk c of row r at c ^ r over the row's chunks) in the
+    // last step's stage -- rows 0..15 in the NB KiB of its A part and rows
+    // 16..31 in the NB KiB of its W part that this wave's own loads fill, so
+    // no other wave touches them -- and reads them back as 8 consecutive
+    // columns per lane.
     if (KT == 1) {
       // a one-step tile: its parameter loads were issued this very step
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -461,21 +508,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
     }
     const int lstage = (step - 1) & 1;  // the stage the tile's last step read
     uint8_t* const Spark = smem + lstage * kStageBytes;
-    float* const E0 = reinterpret_cast<float*>(Spark + wave * 8192);                   // rows 0..15
-    float* const E1 = reinterpret_cast<float*>(Spark + kOperandBytes + wave * 8192);   // rows 16..31
+    float* const E0 = reinterpret_cast<float*>(Spark + wave * NB * 1024);                  // rows 0..15
+    float* const E1 = reinterpret_cast<float*>(Spark + kOperandBytes + wave * NB * 1024);  // rows 16..31
+    // a parked row: HALF floats, CPR groups of 8 columns, 2 CPR 16-byte chunks
+    constexpr int CPR = HALF / 8, CMASK = 2 * CPR - 1, RPS = 64 / CPR, CPR_LOG2 = WB == 4 ? 4 : 3;
+    static_assert((1 << CPR_LOG2) == CPR, "column groups per parked row");
     // The lane index, made opaque to the compiler here: the epilogue's
     // per-lane LDS addresses and store offsets are loop-invariant, and
     // hoisted out of the tile loop they would occupy (and spill) some sixty
     // registers for the whole kernel.
     int elane = lane;
     asm volatile("" : "+v"(elane));
-    const int ec = elane & 15, er = (elane >> 4) & 3;  // read-back role: columns 8 ec .. + 7 of rows er + 4 s
-    const int ecol = wn * 128 + ec * 8;        // within the tile
+    // read-back role: columns 8 ec .. + 7 of rows er + RPS s
+    const int ec = elane & (CPR - 1), er = (elane >> CPR_LOG2) & (RPS - 1);
+    const int ecol = wn * HALF + ec * 8;        // within the tile
     const bool col_ok = cur.n0 + ecol + 8 <= g.N;
     float sc[8], bs[8];
     {
       const float* Psc = reinterpret_cast<const float*>(P);
-      const uint16_t* Pbias = reinterpret_cast<const uint16_t*>(P + BN * 4);
+      const uint16_t* Pbias = reinterpret_cast<const uint16_t*>(P + TILE * 4);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         sc[e] = sa * Psc[ecol + e];
@@ -486,31 +537,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
       }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < WB; ++j) {
       {
         const int r = elane & 31;
         float* const E = r < 16 ? E0 : E1;
         const int rl = r & 15;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < WB; ++i)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int c = i * 8 + 2 * q + ((elane >> 5) & 1);
             v4f v;
             v[0] = acc[i][j][4 * q]; v[1] = acc[i][j][4 * q + 1];
             v[2] = acc[i][j][4 * q + 2]; v[3] = acc[i][j][4 * q + 3];
-            *reinterpret_cast<v4f*>(E + rl * 128 + ((c ^ r) << 2)) = v;
+            *reinterpret_cast<v4f*>(E + rl * HALF + ((c ^ (r & CMASK)) << 2)) = v;
           }
       }
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int s8 = 0; s8 < 8; ++s8) {
-        const int rr = s8 * 4 + er;
+      for (int s8 = 0; s8 < 32 / RPS; ++s8) {
+        const int rr = s8 * RPS + er;
         const float* E = rr < 16 ? E0 : E1;
         const int rl = rr & 15;
-        const v4f lo = *reinterpret_cast<const v4f*>(E + rl * 128 + (((2 * ec) ^ rr) << 2));
-        const v4f hi = *reinterpret_cast<const v4f*>(E + rl * 128 + (((2 * ec + 1) ^ rr) << 2));
+        const v4f lo = *reinterpret_cast<const v4f*>(E + rl * HALF + (((2 * ec) ^ (rr & CMASK)) << 2));
+        const v4f hi = *reinterpret_cast<const v4f*>(E + rl * HALF + (((2 * ec + 1) ^ (rr & CMASK)) << 2));
         // columns 8 ec + 0..7 as bf16 pairs (one conversion instruction each)
         v4u packed;
 #pragma unroll
@@ -520,7 +571,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
           packed[e + 2] = pack_bf16x2_rne(__builtin_fmaf(hi[2 * e], sc[2 * e + 4], bs[2 * e + 4]),
                                           __builtin_fmaf(hi[2 * e + 1], sc[2 * e + 5], bs[2 * e + 5]));
         }
-        const int row = wm * 128 + j * 32 + rr;  // within the tile
+        const int row = wm * HALF + j * 32 + rr;  // within the tile
         if constexpr (VEC) {
           const uint32_t off = col_ok ? (uint32_t)((row * g.ldo + ecol) * 2) : kOutOfRange;
           __builtin_amdgcn_raw_buffer_store_b128(packed, cur.ro, (int)off, 0, 0);
@@ -540,16 +591,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs g, int 
     // of the stage it has just finished reading; then the next step's
     // first-half fragments (their loads landed before the last barrier)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dma_part(lstage, i);
+    for (int i = 0; i < NB; ++i) dma_part(lstage, i);
     advance_load();
     if constexpr (!EXACT) prefetch();
     {
       const uint8_t* An = smem + (step & 1) * kStageBytes;
       const uint8_t* Wn = An + kOperandBytes;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wf0[i] = read_frag(Wn, wn * 128 + i * 32 + frow, fchunk);
+      for (int i = 0; i < WB; ++i) wf0[i] = read_frag(Wn, wn * HALF + i * 32 + frow, fchunk);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) af0[j] = read_frag(An, wm * 128 + j * 32 + frow, fchunk);
+      for (int j = 0; j < WB; ++j) af0[j] = read_frag(An, wm * HALF + j * 32 + frow, fchunk);
     }
   }
   // loads past the last tile still write (zeros) into LDS: let them land
@@ -572,31 +623,55 @@ int cu_count() {
 
 bool gemm_mfma_supported(const GemmArgs& g) {
   // 16-byte vector loads need aligned rows and K % 16 == 0; 32-bit buffer
-  // offsets need a 256-row panel (operands and output) to span less than
-  // 2 GiB.
+  // offsets need a panel of the larger tile (256 rows of the operands and
+  // the output) to span less than 2 GiB.
+  constexpr int64_t kPanelRows = Geo<4>::TILE;
   return ((uintptr_t)g.a % 16 == 0) && ((uintptr_t)g.w % 16 == 0) && (g.lda % 16 == 0) && (g.ldw % 16 == 0) &&
-         (g.K % 16 == 0) && (int64_t)BM * g.lda < (1ll << 31) && (int64_t)BN * g.ldw < (1ll << 31) &&
-         (int64_t)BM * g.ldo * 2 < (1ll << 31) && ((uintptr_t)g.out % 2 == 0) && g.N < (1 << 29);
+         (g.K % 16 == 0) && kPanelRows * g.lda < (1ll << 31) && kPanelRows * g.ldw < (1ll << 31) &&
+         kPanelRows * g.ldo * 2 < (1ll << 31) && ((uintptr_t)g.out % 2 == 0) && g.N < (1 << 29);
 }
 
-template <int FA, int FW>
-hipError_t launch_mfma(const GemmArgs& g, bool fp8_accumulate, hipStream_t stream) {
-  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+template <int WB, int FA, int FW>
+hipError_t launch_mfma_tiles(const GemmArgs& g, bool fp8_accumulate, hipStream_t stream) {
+  constexpr int TILE = Geo<WB>::TILE;
+  const int tiles_m = (g.M + TILE - 1) / TILE, tiles_n = (g.N + TILE - 1) / TILE;
   const int T = tiles_m * tiles_n;
   const unsigned grid = (unsigned)min(T, cu_count());
   const bool vec = (g.N % 8 == 0) && (g.ldo % 8 == 0) && ((uintptr_t)g.out % 16 == 0);
   if (fp8_accumulate) {
     if (vec)
-      gemm_mfma_kernel<false, true, FA, FW><<<grid, kThreads, 0, stream>>>(g, tiles_m, tiles_n);
+      gemm_mfma_kernel<WB, false, true, FA, FW><<<grid, kThreads, 0, stream>>>(g, tiles_m, tiles_n);
     else
-      gemm_mfma_kernel<false, false, FA, FW><<<grid, kThreads, 0, stream>>>(g, tiles_m, tiles_n);
+      gemm_mfma_kernel<WB, false, false, FA, FW><<<grid, kThreads, 0, stream>>>(g, tiles_m, tiles_n);
   } else {
     if (vec)
-      gemm_mfma_kernel<true, true, FA, FW><<<grid, kThreads, 0, stream>>>(g, tiles_m, tiles_n);
+      gemm_mfma_kernel<WB, true, true, FA, FW><<<grid, kThreads, 0, stream>>>(g, tiles_m, tiles_n);
     else
-      gemm_mfma_kernel<true, false, FA, FW><<<grid, kThreads, 0, stream>>>(g, tiles_m, tiles_n);
+      gemm_mfma_kernel<WB, true, false, FA, FW><<<grid, kThreads, 0, stream>>>(g, tiles_m, tiles_n);
   }
   return hipGetLastError();
+}
+
+// Tile size.  Each CU runs one tile at a time.  A 128 x 128 tile (a quarter
+// of the work, four times the DMA loads per product) took 0.45 of a
+// 256 x 256 tile's time with fp32-class sums and 0.58 with fp8 sums (K =
+// 4096).  With fp32-class sums a partial last round of tiles cost about its
+// share (the part is power-limited: CUs left idle let the others clock up),
+// so 128 x 128 tiles run where max(1, tiles / CUs) tile times is the
+// smaller estimate; with fp8 sums partial rounds did not pay (M = 320 on N
+// = 14336: 61 us on 128 x 128 against 50 us on 256 x 256), so 128 x 128
+// tiles run only where they fit one round.  Measured with fp32-class sums:
+// M = 320 to 1024 on N = 4096 went from 80-82 to 36-42 us, M = 2048 on N =
+// 6144 stays on 256 x 256 (98 against 111 us).
+template <int FA, int FW>
+hipError_t launch_mfma(const GemmArgs& g, bool fp8_accumulate, hipStream_t stream) {
+  const int64_t cus = cu_count();
+  const int64_t tiles256 = (int64_t)((g.M + 255) / 256) * ((g.N + 255) / 256);
+  const int64_t tiles128 = (int64_t)((g.M + 127) / 128) * ((g.N + 127) / 128);
+  const bool small = fp8_accumulate ? tiles128 <= cus
+                                    : std::max(cus, tiles128) * 45 < std::max(cus, tiles256) * 100;
+  if (small) return launch_mfma_tiles<2, FA, FW>(g, fp8_accumulate, stream);
+  return launch_mfma_tiles<4, FA, FW>(g, fp8_accumulate, stream);
 }
 
 hipError_t launch_gemm_mfma(const GemmArgs& g, bool fp8_accumulate, hipStream_t stream) {

@@ -175,12 +175,13 @@ fp8_status fp8_quant_dynamic_per_row(const uint16_t* x_bf16, int64_t rows, int64
  *   out    [M, N] bf16, row pitch ldo >= N            (output)
  * M <= 64 runs the skinny (decode) kernel, which streams the weight once
  * (one workgroup serves all rows of M) with no padding or repacking; larger
- * M runs the LDS-staged matrix-core GEMM, except where that GEMM's 256 x 256
- * tiles are too few to occupy the GPU (M <= 256 and N * ceil(M / 64) below
- * 49152, or 32768 with FP8_ACCUM_FP8_MFMA) and for layouts it does not take
- * (rows not 16-byte aligned or K % 16 != 0): there the skinny kernel runs
- * and reads the weight once per 64 rows of M (per 16 rows for unaligned
- * layouts).  Any M, N, K >= 1 is accepted.
+ * M runs the LDS-staged matrix-core GEMM (256 x 256 tiles, or 128 x 128
+ * tiles where the larger ones are too few to occupy the GPU), except for
+ * problems too small for its tiles (M <= 256 and N * ceil(M / 64) below
+ * 20480) and for layouts it does not take (rows not 16-byte aligned or
+ * K % 16 != 0): there the skinny kernel runs and reads the weight once per
+ * 64 rows of M (per 16 rows for unaligned layouts).  Any M, N, K >= 1 is
+ * accepted.
  * Errors: INVALID_ARG for null pointers (bias may be NULL), negative M or
  * N, K < 1, lda/ldw < K, ldo < N, or an unknown scale mode; UNSUPPORTED for
  * M or N >= 2^31, K >= 2^30 or pitches >= 2^40.  M == 0 or N == 0 is an

@@ -109,7 +109,9 @@ def test_mid_m(m, k, n):
 def test_mfma_gemm(m, k, n, pc, accum):
     """The matrix-core GEMM: M > 256, or M of 65 and 256 with N large enough
     that the call does not give the problem to the skinny kernel (one row of
-    tiles, mostly past M for M = 65)."""
+    tiles, mostly past M for M = 65).  All but 1000 x 4096 -> 6144 with fp8
+    sums run 128 x 128 tiles (too few 256 x 256 ones); with fp32-class sums
+    that one runs 384 of them, two on some workgroups."""
     say("mfma", m, k, n, pc, accum)
     d = _prepare(3, m, k, n, per_channel=pc, outliers=pc, rowmul=pc, with_bias=(m % 2 == 0))
     _run_and_check(d, pc, accum=accum)
@@ -117,17 +119,19 @@ def test_mfma_gemm(m, k, n, pc, accum):
 
 @pytest.mark.parametrize("accum", ["fp32", "fp8"])
 @pytest.mark.parametrize("m,k,n", [(65, 4096, 1030), (128, 4096, 4096), (256, 256, 256), (200, 14336, 300),
-                                   (96, 4096, 14336), (256, 4096, 6144)])
-def test_mid_m_problems_too_small_for_the_matrix_core_tiles(m, k, n, accum):
-    """64 < M <= 256 with N * ceil(M / 64) below the matrix-core GEMM's
-    threshold (49152 for fp32-class sums, 32768 for fp8 sums): the skinny
-    kernel runs, in grid rows of 64 rows of M, and sums with fp32-class
-    precision whatever the mode asked for, so both modes meet the fp32
-    bound and give the same bits.  (96 x 4096 -> 14336 crosses over: the
-    skinny kernel with fp32 sums, the matrix-core GEMM with fp8 sums.)"""
+                                   (96, 4096, 8192), (96, 4096, 14336), (256, 4096, 6144), (320, 4096, 4096),
+                                   (1024, 1024, 4100)])
+def test_mid_m_problems_on_each_kernel(m, k, n, accum):
+    """64 < M: problems too small for the matrix-core tiles (M <= 256 and
+    N * ceil(M / 64) < 20480) run on the skinny kernel, in grid rows of 64
+    rows of M, and sum with fp32-class precision whatever the mode asked
+    for (both modes meet the fp32 bound and give the same bits); the others
+    run on the matrix-core GEMM with 128 x 128 tiles (too few 256 x 256
+    ones to occupy the GPU), here M = 96 and 256 on N = 14336 and 6144,
+    M = 320 and 1024 with ragged N."""
     say("mid m", m, k, n, accum)
     d = _prepare(7, m, k, n, per_channel=True, outliers=True, rowmul=True, with_bias=True)
-    skinny = n * ((m + 63) // 64) < (32768 if accum == "fp8" else 49152)
+    skinny = m <= 256 and n * ((m + 63) // 64) < 20480
     out = fp8.scaled_mm(d["a_q"], d["w_q"], d["s_a"], d["s_w"], True, d["bias"], accum=accum)
     torch.cuda.synchronize()
     ref = oracle.scaled_mm(d["aq"], d["wq"], d["sa"], d["sw"], True, d["bias_bits"])
