@@ -636,7 +636,14 @@ hipError_t launch_mfma_tiles(const GemmArgs& g, bool fp8_accumulate, hipStream_t
   constexpr int TILE = Geo<WB>::TILE;
   const int tiles_m = (g.M + TILE - 1) / TILE, tiles_n = (g.N + TILE - 1) / TILE;
   const int T = tiles_m * tiles_n;
-  const unsigned grid = (unsigned)min(T, cu_count());
+  // 128 x 128 tiles: two workgroups fit a CU (128 VGPRs and 64 accumulation
+  // registers per lane of its 512, and 68 KiB of LDS, each; asking the
+  // compiler for two per CU moved the accumulators into VGPRs, within 2-4%
+  // of the same speed), and where the tiles outnumber the CUs
+  // two resident workgroups overlap one's loads with the other's products:
+  // 12-19% faster than one per CU (M = 2048 on N = 4096: 74.6 -> 64.8 us;
+  // M = 320 on N = 14336: 72.6 -> 58.7 us), no change with fewer tiles.
+  const unsigned grid = (unsigned)min(T, (WB == 2 ? 2 : 1) * cu_count());
   const bool vec = (g.N % 8 == 0) && (g.ldo % 8 == 0) && ((uintptr_t)g.out % 16 == 0);
   if (fp8_accumulate) {
     if (vec)
@@ -652,24 +659,22 @@ hipError_t launch_mfma_tiles(const GemmArgs& g, bool fp8_accumulate, hipStream_t
   return hipGetLastError();
 }
 
-// Tile size.  Each CU runs one tile at a time.  A 128 x 128 tile (a quarter
-// of the work, four times the DMA loads per product) took 0.45 of a
-// 256 x 256 tile's time with fp32-class sums and 0.58 with fp8 sums (K =
-// 4096).  With fp32-class sums a partial last round of tiles cost about its
-// share (the part is power-limited: CUs left idle let the others clock up),
-// so 128 x 128 tiles run where max(1, tiles / CUs) tile times is the
-// smaller estimate; with fp8 sums partial rounds did not pay (M = 320 on N
-// = 14336: 61 us on 128 x 128 against 50 us on 256 x 256), so 128 x 128
-// tiles run only where they fit one round.  Measured with fp32-class sums:
-// M = 320 to 1024 on N = 4096 went from 80-82 to 36-42 us, M = 2048 on N =
-// 6144 stays on 256 x 256 (98 against 111 us).
+// Tile size.  Each CU runs one 256 x 256 tile at a time, or two 128 x 128
+// tiles (see launch_mfma_tiles).  A 128 x 128 tile (a quarter of the work,
+// four times the DMA loads per product) took 0.45 of a 256 x 256 tile's
+// time with fp32-class sums and 0.58 with fp8 sums (K = 4096), and a
+// partial last round of tiles cost about its share (the part is
+// power-limited: CUs left idle let the others clock up).  So 128 x 128 tiles
+// run where max(1, tiles / CUs) tile times is the smaller estimate.
+// Measured: M = 320 to 1024 on N = 4096 went from 80-82 to 36-42 us with
+// fp32-class sums and from 47-52 to 28-30 us with fp8 sums; M = 2048 on
+// N = 6144 stays on 256 x 256 (98 against 111 us).
 template <int FA, int FW>
 hipError_t launch_mfma(const GemmArgs& g, bool fp8_accumulate, hipStream_t stream) {
   const int64_t cus = cu_count();
   const int64_t tiles256 = (int64_t)((g.M + 255) / 256) * ((g.N + 255) / 256);
   const int64_t tiles128 = (int64_t)((g.M + 127) / 128) * ((g.N + 127) / 128);
-  const bool small = fp8_accumulate ? tiles128 <= cus
-                                    : std::max(cus, tiles128) * 45 < std::max(cus, tiles256) * 100;
+  const bool small = std::max(cus, tiles128) * (fp8_accumulate ? 58 : 45) < std::max(cus, tiles256) * 100;
   if (small) return launch_mfma_tiles<2, FA, FW>(g, fp8_accumulate, stream);
   return launch_mfma_tiles<4, FA, FW>(g, fp8_accumulate, stream);
 }

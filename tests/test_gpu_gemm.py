@@ -105,13 +105,13 @@ def test_mid_m(m, k, n):
 @pytest.mark.parametrize("accum", ["fp32", "fp8"])
 @pytest.mark.parametrize("m,k,n,pc", [
     (256, 256, 12288, False), (512, 4096, 1024, True), (300, 4096, 4100, False),
-    (777, 1040, 520, True), (65, 128, 24576, False), (1000, 4096, 6144, True)])
+    (777, 1040, 520, True), (65, 128, 24576, False), (1000, 4096, 6144, True), (2048, 1024, 8192, True)])
 def test_mfma_gemm(m, k, n, pc, accum):
     """The matrix-core GEMM: M > 256, or M of 65 and 256 with N large enough
     that the call does not give the problem to the skinny kernel (one row of
-    tiles, mostly past M for M = 65).  All but 1000 x 4096 -> 6144 with fp8
-    sums run 128 x 128 tiles (too few 256 x 256 ones); with fp32-class sums
-    that one runs 384 of them, two on some workgroups."""
+    tiles, mostly past M for M = 65).  All but 2048 x 1024 -> 8192 (256 tiles
+    of 256 x 256) run 128 x 128 tiles, too few 256 x 256 ones; 1000 x 4096 ->
+    6144 runs 384 of them, two workgroups per CU."""
     say("mfma", m, k, n, pc, accum)
     d = _prepare(3, m, k, n, per_channel=pc, outliers=pc, rowmul=pc, with_bias=(m % 2 == 0))
     _run_and_check(d, pc, accum=accum)
