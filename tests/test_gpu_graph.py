@@ -25,7 +25,10 @@ def _eager(x, w_q, s_w, ws, accum):
 
 @pytest.mark.parametrize("m,k,n,accum", [(16, 4096, 1030, "fp32"), (16, 14336, 512, "fp32"),
                                          (300, 1024, 520, "fp32"), (300, 1024, 520, "fp8"),
-                                         (2048, 4096, 1024, "fp32")])
+                                         (2048, 4096, 1024, "fp32"),
+                                         # a mid-M problem on the skinny kernel (two grid rows of M),
+                                         # and 128 x 128 tiles with two workgroups on some CUs
+                                         (128, 4096, 4096, "fp8"), (1024, 1024, 6144, "fp32")])
 def test_graph_replay_matches_eager(m, k, n, accum):
     say("graph", m, k, n, accum)
     w_q, s_w = fp8.quant_weight(dev_bf16(synth.weights(7, n, k, row_multipliers=True)), True)
