@@ -63,6 +63,14 @@ fp8_status check_fmt(const char* fn, fp8_format f) {
 // precision.
 bool few_tiles_for_matrix_cores(int64_t M, int64_t N) { return M <= 256 && N * ((M + 63) / 64) < 20480; }
 
+// From 16 to 64 rows the skinny kernel serves every block of 16 rows of M
+// from one weight step, in time growing with N and the number of blocks; on
+// the widest weights with four blocks one round of the matrix-core GEMM's
+// 128 x 128 tiles is faster (64 x 4096 -> 28672: 52.0 against 45.4 us with
+// fp32-class sums, 52.4 against 41.7 with fp8 sums; at 48 rows the two
+// tie, and on N = 14336 the skinny kernel wins at every M).
+bool wide_enough_for_matrix_cores(int64_t M, int64_t N) { return M > 48 && M <= 64 && N >= 24576; }
+
 // ---- scratch of the no-allocation entry point ----------------------------
 // The dynamic quantization's per-block maxima (quant_workspace_bytes(), the
 // same for every size) live in this array instead of a caller workspace.
@@ -273,8 +281,8 @@ fp8_status fp8_scaled_mm_fmt(const uint8_t* a_q, int64_t lda, fp8_format fmt_a, 
 
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
   const bool fp8_sums = accum == FP8_ACCUM_FP8_MFMA;
-  if (M > 64 && !few_tiles_for_matrix_cores(M, N) && tiles < (1ll << 31) &&
-      fp8w8a8::gemm_mfma_supported(g))
+  if (((M > 64 && !few_tiles_for_matrix_cores(M, N)) || wide_enough_for_matrix_cores(M, N)) &&
+      tiles < (1ll << 31) && fp8w8a8::gemm_mfma_supported(g))
     return hip_status(fp8w8a8::launch_gemm_mfma(g, fp8_sums, s), fn);
 
   // Skinny kernel, in slices of at most 65535 blocks of 16 rows (grid.y).

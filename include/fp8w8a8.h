@@ -79,7 +79,8 @@ typedef enum {
  *                       of 8 products keeping 13 bits below the group's
  *                       largest product, so small products next to large
  *                       ones are truncated.  Where the call runs the skinny
- *                       kernel (M <= 64, small problems up to 256 rows, and
+ *                       kernel (most M <= 64, small problems up to 256
+ *                       rows, and
  *                       layouts the matrix-core GEMM does not take), it sums
  *                       with the FP32 path in either mode.
  */
@@ -173,15 +174,16 @@ fp8_status fp8_quant_dynamic_per_row(const uint16_t* x_bf16, int64_t rows, int64
  *   s_w    1 float (PER_TENSOR) or N floats (PER_CHANNEL) (device)
  *   bias   N bf16 values (device), or NULL for none
  *   out    [M, N] bf16, row pitch ldo >= N            (output)
- * M <= 64 runs the skinny (decode) kernel, which streams the weight once
- * (one workgroup serves all rows of M) with no padding or repacking; larger
- * M runs the LDS-staged matrix-core GEMM (256 x 256 tiles, or 128 x 128
- * tiles where the larger ones are too few to occupy the GPU), except for
- * problems too small for its tiles (M <= 256 and N * ceil(M / 64) below
- * 20480) and for layouts it does not take (rows not 16-byte aligned or
- * K % 16 != 0): there the skinny kernel runs and reads the weight once per
- * 64 rows of M (per 16 rows for unaligned layouts).  Any M, N, K >= 1 is
- * accepted.
+ * Kernels: the skinny (decode) kernel streams the weight once for up to 64
+ * rows of M (one workgroup serves all of them), with no padding or
+ * repacking; the LDS-staged matrix-core GEMM runs 256 x 256 tiles, or
+ * 128 x 128 tiles where the larger ones are too few to occupy the GPU.
+ * M <= 64 runs the skinny kernel, but for 48 < M <= 64 with N >= 24576.
+ * Larger M runs the matrix-core GEMM, but for problems too small for its
+ * tiles (M <= 256 and N * ceil(M / 64) below 20480).  Layouts the
+ * matrix-core GEMM does not take (rows not 16-byte aligned or K % 16 != 0)
+ * run the skinny kernel, which then reads the weight once per 64 rows of M
+ * (per 16 rows for unaligned layouts).  Any M, N, K >= 1 is accepted.
  * Errors: INVALID_ARG for null pointers (bias may be NULL), negative M or
  * N, K < 1, lda/ldw < K, ldo < N, or an unknown scale mode; UNSUPPORTED for
  * M or N >= 2^31, K >= 2^30 or pitches >= 2^40.  M == 0 or N == 0 is an

@@ -120,18 +120,20 @@ def test_mfma_gemm(m, k, n, pc, accum):
 @pytest.mark.parametrize("accum", ["fp32", "fp8"])
 @pytest.mark.parametrize("m,k,n", [(65, 4096, 1030), (128, 4096, 4096), (256, 256, 256), (200, 14336, 300),
                                    (96, 4096, 8192), (96, 4096, 14336), (256, 4096, 6144), (320, 4096, 4096),
-                                   (1024, 1024, 4100)])
+                                   (1024, 1024, 4100), (64, 4096, 28672), (48, 4096, 28672), (57, 1024, 24576)])
 def test_mid_m_problems_on_each_kernel(m, k, n, accum):
-    """64 < M: problems too small for the matrix-core tiles (M <= 256 and
-    N * ceil(M / 64) < 20480) run on the skinny kernel, in grid rows of 64
-    rows of M, and sum with fp32-class precision whatever the mode asked
-    for (both modes meet the fp32 bound and give the same bits); the others
-    run on the matrix-core GEMM with 128 x 128 tiles (too few 256 x 256
-    ones to occupy the GPU), here M = 96 and 256 on N = 14336 and 6144,
-    M = 320 and 1024 with ragged N."""
+    """Around the skinny kernel's bounds: problems too small for the
+    matrix-core tiles (64 < M <= 256 and N * ceil(M / 64) < 20480) run on
+    the skinny kernel in grid rows of 64 rows of M, as do M <= 64 but for
+    48 < M <= 64 with N >= 24576 (the widest weights); the skinny kernel
+    sums with fp32-class precision whatever the mode asked for (both modes
+    meet the fp32 bound and give the same bits).  The others run on the
+    matrix-core GEMM with 128 x 128 tiles (too few 256 x 256 ones to occupy
+    the GPU): M = 96 and 256 on N = 14336 and 6144, M = 320 and 1024 with
+    ragged N, M = 57 and 64 on N of 24576 and 28672."""
     say("mid m", m, k, n, accum)
     d = _prepare(7, m, k, n, per_channel=True, outliers=True, rowmul=True, with_bias=True)
-    skinny = m <= 256 and n * ((m + 63) // 64) < 20480
+    skinny = (m <= 64 and not (m > 48 and n >= 24576)) or (64 < m <= 256 and n * ((m + 63) // 64) < 20480)
     out = fp8.scaled_mm(d["a_q"], d["w_q"], d["s_a"], d["s_w"], True, d["bias"], accum=accum)
     torch.cuda.synchronize()
     ref = oracle.scaled_mm(d["aq"], d["wq"], d["sa"], d["sw"], True, d["bias_bits"])
