@@ -18,10 +18,12 @@
 //   * Both operands are K-contiguous ([M, K] and [N, K]), the matrix cores'
 //     native operand layout: every lane reads 32 contiguous k-bytes of one
 //     row, so no transposition is needed anywhere.
-//   * Persistent: one workgroup per compute unit walks tiles b, b + grid, ...
-//     and the operand pipeline runs across tile boundaries.
+//   * Persistent: one workgroup per compute unit (two with 128 x 128 tiles)
+//     walks tiles b, b + grid, ... and the operand pipeline runs across tile
+//     boundaries.
 //   * Global -> LDS directly (buffer_load ... lds, no staging registers),
-//     two stages of 64 KiB.  Out-of-range lanes (rows past M or N, k past
+//     two stages of 64 KiB (32 KiB with 128 x 128 tiles).  Out-of-range
+//     lanes (rows past M or N, k past
 //     K) return zeros through the buffer range check, so edge tiles need no
 //     branches and k tails add nothing.
 //   * One barrier per k step, in its middle.  A step's products are split
