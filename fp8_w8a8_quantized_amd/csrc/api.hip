@@ -285,15 +285,23 @@ fp8_status fp8_scaled_mm_fmt(const uint8_t* a_q, int64_t lda, fp8_format fmt_a, 
       tiles < (1ll << 31) && fp8w8a8::gemm_mfma_supported(g))
     return hip_status(fp8w8a8::launch_gemm_mfma(g, fp8_sums, s), fn);
 
-  // Skinny kernel, in slices of at most 65535 blocks of 16 rows (grid.y).
-  const int64_t slice = 65535ll * 16;
-  for (int64_t m0 = 0; m0 < M; m0 += slice) {
-    fp8w8a8::GemmArgs gs = g;
-    gs.a = a_q + m0 * lda;
-    gs.out = out_bf16 + m0 * ldo;
-    gs.M = (int32_t)((M - m0) < slice ? (M - m0) : slice);
-    fp8_status st = hip_status(fp8w8a8::launch_gemm_skinny(gs, s), fn);
-    if (st != FP8_OK) return st;
+  // Skinny kernel, in slices of at most 65535 blocks of 16 rows (grid.y) and
+  // 2^25 columns (a launch's threads along x must stay below 2^32: at most
+  // 2^21 workgroups of up to 1024 threads).
+  const int64_t slice_m = 65535ll * 16, slice_n = 1ll << 25;
+  for (int64_t n0 = 0; n0 < N; n0 += slice_n) {
+    for (int64_t m0 = 0; m0 < M; m0 += slice_m) {
+      fp8w8a8::GemmArgs gs = g;
+      gs.a = a_q + m0 * lda;
+      gs.w = w_q + n0 * ldw;
+      gs.s_w = g.per_channel ? s_w + n0 : s_w;
+      gs.bias = bias_bf16 != nullptr ? bias_bf16 + n0 : nullptr;
+      gs.out = out_bf16 + m0 * ldo + n0;
+      gs.M = (int32_t)((M - m0) < slice_m ? (M - m0) : slice_m);
+      gs.N = (int32_t)((N - n0) < slice_n ? (N - n0) : slice_n);
+      fp8_status st = hip_status(fp8w8a8::launch_gemm_skinny(gs, s), fn);
+      if (st != FP8_OK) return st;
+    }
   }
   return FP8_OK;
 }

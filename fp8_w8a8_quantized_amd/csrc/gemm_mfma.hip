@@ -636,7 +636,8 @@ bool gemm_mfma_supported(const GemmArgs& g) {
 template <int WB, int FA, int FW>
 hipError_t launch_mfma_tiles(const GemmArgs& g, bool fp8_accumulate, hipStream_t stream) {
   constexpr int TILE = Geo<WB>::TILE;
-  const int tiles_m = (g.M + TILE - 1) / TILE, tiles_n = (g.N + TILE - 1) / TILE;
+  // in 64 bits: M may come within a tile of 2^31
+  const int tiles_m = (int)(((int64_t)g.M + TILE - 1) / TILE), tiles_n = (int)(((int64_t)g.N + TILE - 1) / TILE);
   const int T = tiles_m * tiles_n;
   // 128 x 128 tiles: two workgroups fit a CU (128 VGPRs and 64 accumulation
   // registers per lane of its 512, and 68 KiB of LDS, each; asking the
@@ -674,8 +675,9 @@ hipError_t launch_mfma_tiles(const GemmArgs& g, bool fp8_accumulate, hipStream_t
 template <int FA, int FW>
 hipError_t launch_mfma(const GemmArgs& g, bool fp8_accumulate, hipStream_t stream) {
   const int64_t cus = cu_count();
-  const int64_t tiles256 = (int64_t)((g.M + 255) / 256) * ((g.N + 255) / 256);
-  const int64_t tiles128 = (int64_t)((g.M + 127) / 128) * ((g.N + 127) / 128);
+  const int64_t M = g.M, N = g.N;
+  const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
   const bool small = std::max(cus, tiles128) * (fp8_accumulate ? 58 : 45) < std::max(cus, tiles256) * 100;
   if (small) return launch_mfma_tiles<2, FA, FW>(g, fp8_accumulate, stream);
   return launch_mfma_tiles<4, FA, FW>(g, fp8_accumulate, stream);

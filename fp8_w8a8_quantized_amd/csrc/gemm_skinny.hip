@@ -735,7 +735,7 @@ hipError_t launch_skinny(const GemmArgs& g, hipStream_t stream) {
   const bool aligned = ((uintptr_t)g.a % 16 == 0) && ((uintptr_t)g.w % 16 == 0) && (g.lda % 16 == 0) &&
                        (g.ldw % 16 == 0) && (g.K % 16 == 0) && g.lda < kMaxPitch && g.ldw < kMaxPitch &&
                        g.N < (1 << 29) && (g.M <= 16 || g.lda < kMaxPitchMB);
-  const int64_t tiles_n = (g.N + 15) / 16, tiles_m = (g.M + 15) / 16;
+  const int64_t tiles_n = ((int64_t)g.N + 15) / 16, tiles_m = ((int64_t)g.M + 15) / 16;  // N may come near 2^31
   dim3 grid((unsigned)tiles_n, (unsigned)tiles_m);
   if (aligned && g.M > 16) return launch_skinny_mb<FA, FW>(g, stream);
   if (aligned) {

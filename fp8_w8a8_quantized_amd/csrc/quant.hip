@@ -407,17 +407,19 @@ __global__ __launch_bounds__(256) void quant_static_kernel(QuantArgs a, PlainSrc
   quant_range<F>(a, src, blockIdx.x * blockDim.x + threadIdx.x, a.total_units, gridDim.x * blockDim.x, s);
 }
 
-// One workgroup per row: the row's own amax and scale, then its codes.
+// One workgroup per row at a time (rows b, b + gridDim.x, ...): the row's
+// own amax and scale, then its codes.
 template <int F>
 __global__ __launch_bounds__(256) void quant_per_row_kernel(QuantArgs a, PlainSrc src, float* scales_out) {
   __shared__ uint32_t red[16];
-  const uint32_t r = blockIdx.x;
-  const uint32_t u0 = r * a.units_per_row, u1 = u0 + a.units_per_row;
-  uint32_t m = absmax_range(a, src, u0 + threadIdx.x, u1, blockDim.x);
-  m = block_max_u32(m, red);
-  const float s = scale_from_amax<F>(bf16_to_f32(m));
-  if (threadIdx.x == 0) scales_out[r] = s;
-  quant_range<F>(a, src, u0 + threadIdx.x, u1, blockDim.x, s);
+  for (uint32_t r = blockIdx.x; r < a.rows; r += gridDim.x) {
+    const uint32_t u0 = r * a.units_per_row, u1 = u0 + a.units_per_row;
+    uint32_t m = absmax_range(a, src, u0 + threadIdx.x, u1, blockDim.x);
+    m = block_max_u32(m, red);
+    const float s = scale_from_amax<F>(bf16_to_f32(m));
+    if (threadIdx.x == 0) scales_out[r] = s;
+    quant_range<F>(a, src, u0 + threadIdx.x, u1, blockDim.x, s);
+  }
 }
 
 // Residual add, RMS statistics and the absmax of the normalized values, for
@@ -512,6 +514,7 @@ PlainSrc plain_src(const uint16_t* x, int64_t ld_x) { return PlainSrc{x, ld_x, r
 
 constexpr uint32_t kPartialBlocks = 1024;         // max blocks of the two-launch path
 constexpr uint32_t kSmallUnits = 1u << 14;        // <= 128 Ki elements (256 KiB): one launch
+constexpr uint32_t kPerRowBlocks = 1u << 20;      // max blocks of the per-row quantization
 
 uint32_t grid_for_units(uint32_t units, uint32_t per_block, uint32_t cap) {
   uint32_t g = (units + per_block - 1) / per_block;
@@ -639,10 +642,13 @@ hipError_t launch_quant_per_row(const uint16_t* x, int64_t rows, int64_t cols, i
     return hipGetLastError();
   }
   QuantArgs a = make_args(rows, cols, q, ld_q);
+  // a launch's threads must stay below 2^32: past 2^20 rows the workgroups
+  // take several rows each
+  const uint32_t grid = (uint32_t)min(rows, (int64_t)kPerRowBlocks);
   if (fmt == kE5M2)
-    quant_per_row_kernel<kE5M2><<<(uint32_t)rows, 256, 0, stream>>>(a, plain_src(x, ld_x), scales_out);
+    quant_per_row_kernel<kE5M2><<<grid, 256, 0, stream>>>(a, plain_src(x, ld_x), scales_out);
   else
-    quant_per_row_kernel<kE4M3><<<(uint32_t)rows, 256, 0, stream>>>(a, plain_src(x, ld_x), scales_out);
+    quant_per_row_kernel<kE4M3><<<grid, 256, 0, stream>>>(a, plain_src(x, ld_x), scales_out);
   return hipGetLastError();
 }
 

@@ -295,6 +295,88 @@ def test_output_past_4_gib_sampled_rows(k):
     assert_gemm_close(ob, ref, d["aq"][rows], d["sa"], d["wq"], d["sw"], True, bias_bits=d["bias_bits"])
 
 
+def _device_codes(gen, shape):
+    """Uniformly random finite e4m3 codes drawn on the device (the NaN codes
+    0x7F and 0xFF become 0), filled 1 GiB at a time."""
+    t = torch.empty(shape, dtype=torch.uint8, device="cuda")
+    flat = t.view(-1)
+    for i in range(0, flat.numel(), 1 << 30):
+        sl = flat[i:i + (1 << 30)]
+        sl.random_(0, 256, generator=gen)
+        sl.masked_fill_((sl & 0x7F) == 0x7F, 0)
+    return t
+
+
+@pytest.mark.timeout(600)
+def test_rows_up_to_2_pow_31_on_the_matrix_core_kernel():
+    """M = 2^31 - 1, the most rows the call takes (K = 16, N = 8: 32 GiB of
+    activation codes and a 32 GiB output).  Counting the tiles adds up to a
+    tile's rows to M, past 2^31, so it has to run in 64 bits.  fp32-class sums
+    run 128 x 128 tiles here and fp8 sums 256 x 256 ones, so both tile sizes
+    are covered.  Rows at the start, around 2^30 and in the last (ragged)
+    tiles are checked against the oracle."""
+    m, k, n = (1 << 31) - 1, 16, 8
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(21)
+    a_q = _device_codes(gen, (m, k))
+    torch.cuda.synchronize()
+    rows = np.array(sorted({0, 1, 127, 128, 255, 256, (1 << 30) - 1, 1 << 30, m - 257, m - 256, m - 255,
+                            m - 128, m - 127, m - 2, m - 1}))
+    say("M = 2^31 - 1", m, k, n, "sampled rows", rows.tolist())
+    idx = torch.from_numpy(rows).cuda()
+    aq_rows = host_u8(a_q[idx])
+    w = synth.weights(11, n, k, row_multipliers=True)
+    b = synth.bias(11, n)
+    w_q, s_w = fp8.quant_weight(dev_bf16(w), True)
+    wq_ref, sw_ref = oracle.quant_weight(w, True)
+    s_a = torch.tensor([0.0625], dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    assert np.array_equal(host_f32(s_w), sw_ref) and np.array_equal(host_u8(w_q), wq_ref)
+    ref = oracle.scaled_mm(aq_rows, wq_ref, np.float32(0.0625), sw_ref, True, b)
+    for accum in ("fp32", "fp8"):
+        say("  accumulation", accum)
+        out = fp8.scaled_mm(a_q, w_q, s_a, s_w, True, dev_bf16(b), accum=accum)
+        torch.cuda.synchronize()
+        ob = host_bf16_bits(out[idx])
+        del out
+        assert_gemm_close(ob, ref, aq_rows, np.float32(0.0625), wq_ref, sw_ref, True, bias_bits=b, accum=accum)
+
+
+@pytest.mark.timeout(600)
+def test_columns_up_to_2_pow_31_on_the_skinny_kernel():
+    """N = 2^31 - 1, the most output columns the call takes (M = 2, K = 2:
+    the byte-granular skinny kernel; 4 GiB of weight codes, per-channel
+    scales (8 GiB), a bias (4 GiB) and an 8 GiB output).  The call runs in
+    column slices of 2^25, since one launch's threads must stay below 2^32,
+    and counts its column blocks in 64 bits.  Columns at the start, at slice
+    boundaries, around 2^30 and in the last (ragged) block are checked
+    against the oracle."""
+    m, k, n = 2, 2, (1 << 31) - 1
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(22)
+    w_q = _device_codes(gen, (n, k))
+    s_w = torch.empty(n, dtype=torch.float32, device="cuda").uniform_(0.25, 4.0, generator=gen)
+    bias = torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_(generator=gen)
+    torch.cuda.synchronize()
+    cols = np.array(sorted({0, 1, 15, 16, (1 << 25) - 1, 1 << 25, (1 << 25) + 1, (1 << 30) - 1, 1 << 30,
+                            n - 17, n - 16, n - 15, n - 2, n - 1}))
+    say("N = 2^31 - 1", m, k, n, "sampled columns", cols.tolist())
+    idx = torch.from_numpy(cols).cuda()
+    wq_cols = host_u8(w_q[idx])
+    sw_cols = host_f32(s_w[idx])
+    b_cols = host_bf16_bits(bias[idx])
+    codes = np.arange(256, dtype=np.uint8)
+    codes = codes[(codes & 0x7F) != 0x7F]
+    aq = np.random.default_rng(22).choice(codes, size=(m, k)).astype(np.uint8)
+    s_a = torch.tensor([0.5], dtype=torch.float32, device="cuda")
+    out = fp8.scaled_mm(torch.from_numpy(aq).cuda(), w_q, s_a, s_w, True, bias)
+    torch.cuda.synchronize()
+    ob = host_bf16_bits(out[:, idx])
+    del out
+    ref = oracle.scaled_mm(aq, wq_cols, np.float32(0.5), sw_cols, True, b_cols)
+    assert_gemm_close(ob, ref, aq, np.float32(0.5), wq_cols, sw_cols, True, bias_bits=b_cols)
+
+
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("m,n", [(13, 130), (40, 72), (300, 520)])
 def test_longest_k_the_oracle_sums_exactly(m, n):

@@ -244,3 +244,26 @@ def test_quantizers_past_4_gib_sampled_rows():
     q_ref, s_rows_ref = oracle.quant_weight(xs, True)
     assert np.array_equal(host_f32(s_rows)[sample], s_rows_ref)
     assert np.array_equal(host_u8(q[sample]), q_ref)
+
+
+@pytest.mark.timeout(300)
+def test_per_row_quantizer_past_2_pow_24_rows():
+    """16,777,221 rows of 16 (512 MiB of bf16): one 256-thread workgroup per
+    row would pass 2^32 threads in one launch, so past 2^20 rows each
+    workgroup takes several rows.  Rows on both sides of the 2^20 and 2^24
+    marks (the first rows handled by a workgroup's second and 17th turn),
+    the first and the last rows are compared with the oracle: codes and
+    scales bit for bit."""
+    rows, cols = (1 << 24) + 5, 16
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(23)
+    x = torch.randn((rows, cols), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    sample = sorted({0, 1, rows - 2, rows - 1, *[r + d for r in (1 << 20, 1 << 24) for d in (-1, 0, 1)]})
+    say("per-row quantizer, rows", rows, "sampled", sample)
+    xs = host_bf16_bits(x[sample])
+    q, s_rows = fp8.quant_weight(x, True)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_weight(xs, True)
+    assert np.array_equal(host_f32(s_rows[sample]), s_ref)
+    assert np.array_equal(host_u8(q[sample]), q_ref)
