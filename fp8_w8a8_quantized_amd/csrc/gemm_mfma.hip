@@ -1,5 +1,6 @@
-// Scaled FP8 GEMM on the gfx950 matrix cores for M > 64 (prefill), with the
-// rescale epilogue fused into the store.
+// Scaled FP8 GEMM on the gfx950 matrix cores for M > 64 (prefill; also 49
+// to 64 rows on the widest weights), with the rescale epilogue fused into
+// the store.
 //
 // out[m, n] = bf16( sum_k A[m, k] * W[n, k] * (s_a * s_w[n]) + bias[n] ):
 // the W8A8 linear of "Prototype FP8Linear W8A8 runtime quantization"
@@ -23,9 +24,8 @@
 //     boundaries.
 //   * Global -> LDS directly (buffer_load ... lds, no staging registers),
 //     two stages of 64 KiB (32 KiB with 128 x 128 tiles).  Out-of-range
-//     lanes (rows past M or N, k past
-//     K) return zeros through the buffer range check, so edge tiles need no
-//     branches and k tails add nothing.
+//     lanes (rows past M or N, k past K) return zeros through the buffer
+//     range check, so edge tiles need no branches and k tails add nothing.
 //   * One barrier per k step, in its middle.  A step's products are split
 //     in two halves of 64 k.  Before the barrier the wave multiplies the
 //     first half (whose fragments it read during the previous step) and

@@ -38,8 +38,9 @@
 //
 // M from 17 to 64 runs a multi-block variant in which one workgroup serves
 // every 16-row block of M (up to four) from each weight step, so the weight
-// still streams once; larger M on this path (layouts the matrix-core GEMM
-// does not take) uses grid rows of 64.  Layouts that are not 16-byte
+// still streams once; larger M on this path (problems of up to 256 rows too
+// small for the matrix-core GEMM's tiles, and layouts that kernel does not
+// take) uses grid rows of 64.  Layouts that are not 16-byte
 // aligned (or K % 16 != 0) use a byte-granular variant that loads each
 // lane's 32 bytes directly in the matrix-core layout, one 16-row block of M
 // per grid row.
