@@ -63,13 +63,16 @@ fp8_status check_fmt(const char* fn, fp8_format f) {
 // precision.
 bool few_tiles_for_matrix_cores(int64_t M, int64_t N) { return M <= 256 && N * ((M + 63) / 64) < 20480; }
 
-// From 16 to 64 rows the skinny kernel serves every block of 16 rows of M
-// from one weight step, in time growing with N and the number of blocks; on
-// the widest weights with four blocks one round of the matrix-core GEMM's
-// 128 x 128 tiles is faster (64 x 4096 -> 28672: 52.0 against 45.4 us with
-// fp32-class sums, 52.4 against 41.7 with fp8 sums; at 48 rows the two
-// tie, and on N = 14336 the skinny kernel wins at every M).
-bool wide_enough_for_matrix_cores(int64_t M, int64_t N) { return M > 48 && M <= 64 && N >= 24576; }
+// From 17 to 64 rows the skinny kernels serve every block of 16 rows of M
+// from one weight step (on wide weights the wide variant, whose workgroups
+// load each activation step once for four weight blocks), in time growing
+// with N and the number of blocks.  Past 48 rows the matrix-core GEMM's
+// 128 x 128 tiles take one round per 2 x CUs tiles, about 44 us for a round
+// at K = 4096; the skinny kernel is faster up to N of some 40k (64 x 4096 ->
+// 28672: 39 against 44.8 us with fp32-class sums, 39.6-40.2 against 41.7-42.1
+// with fp8 sums), the matrix-core GEMM from two rounds on (64 x 4096 ->
+// 57344: 64.4 against 69.0 us).
+bool wide_enough_for_matrix_cores(int64_t M, int64_t N) { return M > 48 && M <= 64 && N >= 57344; }
 
 // ---- scratch of the no-allocation entry point ----------------------------
 // The dynamic quantization's per-block maxima (quant_workspace_bytes(), the

@@ -40,7 +40,10 @@
 // every 16-row block of M (up to four) from each weight step, so the weight
 // still streams once; larger M on this path (problems of up to 256 rows too
 // small for the matrix-core GEMM's tiles, and layouts that kernel does not
-// take) uses grid rows of 64.  Layouts that are not 16-byte
+// take) uses grid rows of 64.  On wide weights, M from 17 to 64 runs a wide
+// variant instead: each wave owns a weight block over the whole of K and the
+// workgroup loads each activation step once for its four blocks, so fewer
+// activation lines pass the texture path per weight line.  Layouts that are not 16-byte
 // aligned (or K % 16 != 0) use a byte-granular variant that loads each
 // lane's 32 bytes directly in the matrix-core layout, one 16-row block of M
 // per grid row.
@@ -666,6 +669,141 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_mb_kernel(GemmArgs g) {
   }
 }
 
+// Wide weights at small M: each of the 4 waves owns its own 16-row weight
+// block (64 rows per workgroup) and walks the whole of K, so no partial
+// tiles are summed across waves.  The activation rows of a step are loaded
+// once per workgroup -- wave b loads the step of M block b -- into a shared
+// LDS area double-buffered by step parity, and every wave multiplies its
+// weight block with all of them: per weight line the texture path moves
+// MB / 4 activation lines instead of MB (the multi-block kernel) or 1 / 2
+// (the two-block kernel).  One workgroup barrier per step orders the shared
+// area: a step's blocks are complete at it, and a wave writes a buffer again
+// two steps later only after every wave has passed the barrier that follows
+// its reads of it.  Waves whose block starts past N load nothing (a resource
+// of size 0) and store nothing.
+template <int MB, int D, bool NT, int FA, int FW>
+__global__ __launch_bounds__(256) void gemm_skinny_wide_kernel(GemmArgs g) {
+  static_assert(MB >= 1 && MB <= 4, "one loading wave per block of M");
+  __shared__ __attribute__((aligned(16))) uint8_t wstage[4][16 * 256];
+  __shared__ __attribute__((aligned(16))) uint8_t astage[2][MB][16 * 256];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 15, grp = lane >> 4;
+  const int n0 = blockIdx.x * 64 + wave * 16, m0 = blockIdx.y * (16 * MB);
+  const int steps = (g.K + 255) >> 8;
+  const int lr = lane >> 4, lc = (lane & 15) * 16;
+  const int rows_w = max(min(g.N - n0, 16), 0), rows_a = min(g.M - m0, 16 * MB);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.w + (int64_t)min(n0, g.N - 1) * g.ldw), (short)0, (int)(rows_w * g.ldw), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.a + (int64_t)m0 * g.lda), (short)0, (int)(rows_a * g.lda), kRsrcWord3);
+  const uint32_t ldw = (uint32_t)g.ldw, lda = (uint32_t)g.lda;
+  // this wave's weight rows, and the rows of its M block (waves >= MB load none)
+  uint32_t wo[4], ao[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t row = 4 * j + lr;
+    wo[j] = (int)row < rows_w ? row * ldw + lc : kOutOfRange;
+    const uint32_t rowa = 16 * wave + row;
+    ao[j] = wave < MB && (int)rowa < rows_a ? rowa * lda + lc : kOutOfRange;
+  }
+  uint8_t* LW = wstage[wave];
+  const int swz_w = (lane & 15);
+
+  v4i wv[D][4], av[D][4];
+  auto issue = [&](int slot, int i) {  // step i
+    const int k0 = i * 256;
+    const bool kin = i < steps && k0 + lc < g.K;
+    uint32_t ow[4], oa[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ow[j] = kin ? wo[j] + k0 : kOutOfRange;
+      oa[j] = kin ? ao[j] + k0 : kOutOfRange;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      wv[slot][j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rw, ow[j], 0, NT ? kNonTemporal : 0));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      av[slot][j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, oa[j], 0, 0));
+  };
+  __builtin_amdgcn_sched_barrier(0);
+  const EpiParams ep = load_epi_params(g, lane, min(n0, g.N - 1));
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d) {
+    issue(d, d);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  v4f acc[MB];
+#pragma unroll
+  for (int b = 0; b < MB; ++b) acc[b] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < steps; i += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      issue((d + D - 1) % D, i + d + D - 1);
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(8 * (D - 1)));
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + d < steps) {  // the same for every wave of the workgroup
+        uint8_t(*const AS)[16 * 256] = astage[(i + d) & 1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = 4 * j + lr;
+          *reinterpret_cast<v4i*>(LW + row * 256 + ((swz_w ^ row) << 4)) = wv[d][j];
+          if (wave < MB) *reinterpret_cast<v4i*>(AS[wave] + row * 256 + ((swz_w ^ row) << 4)) = av[d][j];
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int c0 = t * 8 + grp, c1 = t * 8 + 4 + grp;
+          const v8i wf = cat8(*reinterpret_cast<const v4i*>(LW + r * 256 + ((c0 ^ r) << 4)),
+                              *reinterpret_cast<const v4i*>(LW + r * 256 + ((c1 ^ r) << 4)));
+          bf16x8 wb[4];  // the weight fragment converted once for every block
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            fp8x4_to_bf16<FW>(wf[2 * u], wb[u], 0);
+            fp8x4_to_bf16<FW>(wf[2 * u + 1], wb[u], 4);
+          }
+#pragma unroll
+          for (int b = 0; b < MB; ++b) {
+            const uint8_t* LA = AS[b];
+            const v8i af = cat8(*reinterpret_cast<const v4i*>(LA + r * 256 + ((c0 ^ r) << 4)),
+                                *reinterpret_cast<const v4i*>(LA + r * 256 + ((c1 ^ r) << 4)));
+            acc[b] = mfma_bf16w_fp8a<FA>(wb, af, acc[b]);
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+  }
+  if (n0 >= g.N) return;
+  const float sa = *g.s_a;
+  const int nb = n0 + 4 * grp;
+#pragma unroll
+  for (int b = 0; b < MB; ++b) {
+    const int m = m0 + 16 * b + (lane & 15);
+    if (m >= g.M) break;
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = f32_to_bf16_rne(__builtin_fmaf(acc[b][i], sa * ep.sw[i], bf16_to_f32(ep.bias[i])));
+    uint16_t* orow = g.out + (int64_t)m * g.ldo;
+    if (nb + 3 < g.N && ((uintptr_t)(orow + nb) % 8) == 0) {
+      uint2 v;
+      v.x = o[0] | (o[1] << 16);
+      v.y = o[2] | (o[3] << 16);
+      *reinterpret_cast<uint2*>(orow + nb) = v;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (nb + i < g.N) orow[nb + i] = (uint16_t)o[i];
+    }
+  }
+}
+
 template <int NW, int U, bool VEC, int FA, int FW>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_generic_kernel(GemmArgs g) {
   __shared__ float red[NW][4][64];
@@ -731,6 +869,41 @@ hipError_t launch_skinny_mb(const GemmArgs& g, hipStream_t stream) {
   }
 }
 
+// The wide kernel (16 < M <= 64) where it measured faster than the
+// multi-block kernel: M > 32 with N >= 56 x CUs, or M > 16 with N >= 112 x
+// CUs (N / 64 workgroups, one per CU or more).  Per-channel GEMMs with
+// K = 4096, weights streaming from HBM, alternating runs: N = 14336 at
+// M = 33-64 8-19% faster (64 rows: 29.9 -> 24.3 us), N = 28672 at M = 17-48
+// 7-22% faster, N = 57344 5-26%; at N = 8192 (128 workgroups) 30-58%
+// slower, at N = 14336 with M <= 32 and N = 24576 with M = 17 within 5%
+// either way.  Two steps in flight beat three.
+bool use_wide(int64_t M, int64_t N) {
+  const int64_t cus = device_cus();
+  return M > 16 && M <= 64 && ((M > 32 && N >= 56 * cus) || N >= 112 * cus);
+}
+constexpr int kWideDepth = 2;
+
+template <int MB, int FA, int FW>
+hipError_t launch_wide_mb(const GemmArgs& g, hipStream_t stream) {
+  const bool nt = (int64_t)g.N * g.K >= (int64_t(32) << 20);
+  const dim3 grid((unsigned)((g.N + 63) / 64), 1);
+  if (nt)
+    gemm_skinny_wide_kernel<MB, kWideDepth, true, FA, FW><<<grid, 256, 0, stream>>>(g);
+  else
+    gemm_skinny_wide_kernel<MB, kWideDepth, false, FA, FW><<<grid, 256, 0, stream>>>(g);
+  return hipGetLastError();
+}
+
+template <int FA, int FW>
+hipError_t launch_wide(const GemmArgs& g, hipStream_t stream) {
+  switch ((g.M + 15) / 16) {
+    case 1: return launch_wide_mb<1, FA, FW>(g, stream);
+    case 2: return launch_wide_mb<2, FA, FW>(g, stream);
+    case 3: return launch_wide_mb<3, FA, FW>(g, stream);
+    default: return launch_wide_mb<4, FA, FW>(g, stream);
+  }
+}
+
 template <int FA, int FW>
 hipError_t launch_skinny(const GemmArgs& g, hipStream_t stream) {
   const bool aligned = ((uintptr_t)g.a % 16 == 0) && ((uintptr_t)g.w % 16 == 0) && (g.lda % 16 == 0) &&
@@ -738,6 +911,7 @@ hipError_t launch_skinny(const GemmArgs& g, hipStream_t stream) {
                        g.N < (1 << 29) && (g.M <= 16 || g.lda < kMaxPitchMB);
   const int64_t tiles_n = ((int64_t)g.N + 15) / 16, tiles_m = ((int64_t)g.M + 15) / 16;  // N may come near 2^31
   dim3 grid((unsigned)tiles_n, (unsigned)tiles_m);
+  if (aligned && use_wide(g.M, g.N)) return launch_wide<FA, FW>(g, stream);
   if (aligned && g.M > 16) return launch_skinny_mb<FA, FW>(g, stream);
   if (aligned) {
     // Interleaved steps for long K (>= 8192), contiguous ranges otherwise;

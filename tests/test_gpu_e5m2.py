@@ -80,7 +80,9 @@ def _gemm_case(m, k, n, fa, fw, per_channel, accum, seed):
 @pytest.mark.parametrize("m,k,n", [(16, 4096, 1030), (3, 4096, 4100), (7, 1000, 33), (40, 4096, 300),
                                    # K >= 8192 (interleaved K steps) and/or >= 32 MiB of weights
                                    # (non-temporal loads): every variant of the skinny kernel
-                                   (3, 8208, 257), (4, 8192, 4100), (5, 4096, 8200), (6, 2048, 16400)])
+                                   (3, 8208, 257), (4, 8192, 4100), (5, 4096, 8200), (6, 2048, 16400),
+                                   # 16 < M <= 64 on wide weights: the wide kernel (on a 256-CU part)
+                                   (20, 1024, 28680), (36, 1024, 14400)])
 def test_e5m2_skinny_gemm(fa, fw, m, k, n):
     say("e5m2 skinny", fa, fw, m, k, n)
     _gemm_case(m, k, n, fa, fw, True, "fp32", 64)

@@ -101,6 +101,47 @@ def test_mid_m(m, k, n):
     _run_and_check(d, False)
 
 
+# ------------------------------------- wide skinny kernel (16 < M <= 64, wide N)
+@pytest.mark.parametrize("m,k,n,pc,bias", [
+    (33, 4096, 14336, True, True),    # M > 32, N = 56 x CUs: one row in the third block of M
+    (40, 1024, 14400, False, False),  # plain weight loads (under 32 MiB), per-tensor
+    (64, 2048, 14344, True, True),    # the last workgroup: wave 0 holds 8 rows, waves 1-3 start past N
+    (17, 4096, 28672, True, False),   # M > 16, N = 112 x CUs: one row in the second block
+    (24, 1040, 28680, False, True),   # a ragged k step (K = 4 x 256 + 16)
+    (48, 4096, 28676, True, True),    # N % 8 == 4: 8-byte stores, the last columns element by element
+    (63, 4096, 14339, True, True),    # odd N: every row of the last block element by element
+])
+def test_wide_skinny_kernel(m, k, n, pc, bias):
+    """The wide skinny kernel (each wave its own 16-row weight block over all
+    of K, the activation steps shared through LDS; on a 256-CU part it runs
+    for M > 32 with N >= 14336 and for M > 16 with N >= 28672): ragged M, N
+    and K, per-tensor and per-channel scales, with and without bias."""
+    say("wide skinny", m, k, n, pc, bias)
+    d = _prepare(9, m, k, n, per_channel=pc, outliers=pc, rowmul=pc, with_bias=bias)
+    _run_and_check(d, pc)
+
+
+@pytest.mark.parametrize("m,n", [(32, 14336), (33, 14336), (33, 14335), (16, 28672), (17, 28672), (17, 28671)])
+def test_wide_skinny_kernel_bounds(m, n):
+    """Both sides of the wide kernel's bounds (on a 256-CU part): 33 x 14336
+    and 17 x 28672 run it; M = 32 and N = 14335 stay on the multi-block
+    kernel, M = 16 on the two-block kernel, N = 28671 with M = 17 on the
+    multi-block kernel.  Pitched operands and output (the kernels index rows
+    by pitch, not by K or N)."""
+    k = 1024
+    say("wide bounds", m, k, n)
+    d = _prepare(9, m, k, n, per_channel=True, rowmul=True, with_bias=True, sub=m)
+    a = torch.zeros((m, k + 48), dtype=torch.uint8, device="cuda")
+    a[:, :k] = d["a_q"]
+    w = torch.zeros((n, k + 32), dtype=torch.uint8, device="cuda")
+    w[:, :k] = d["w_q"]
+    out = torch.zeros((m, n + 24), dtype=torch.bfloat16, device="cuda")[:, :n]
+    fp8.scaled_mm(a[:, :k], w[:, :k], d["s_a"], d["s_w"], True, d["bias"], out=out)
+    torch.cuda.synchronize()
+    ref = oracle.scaled_mm(d["aq"], d["wq"], d["sa"], d["sw"], True, d["bias_bits"])
+    assert_gemm_close(host_bf16_bits(out), ref, d["aq"], d["sa"], d["wq"], d["sw"], True, bias_bits=d["bias_bits"])
+
+
 # ------------------------------ matrix-core GEMM (M > 64 with enough output tiles)
 @pytest.mark.parametrize("accum", ["fp32", "fp8"])
 @pytest.mark.parametrize("m,k,n,pc", [
@@ -120,20 +161,22 @@ def test_mfma_gemm(m, k, n, pc, accum):
 @pytest.mark.parametrize("accum", ["fp32", "fp8"])
 @pytest.mark.parametrize("m,k,n", [(65, 4096, 1030), (128, 4096, 4096), (256, 256, 256), (200, 14336, 300),
                                    (96, 4096, 8192), (96, 4096, 14336), (256, 4096, 6144), (320, 4096, 4096),
-                                   (1024, 1024, 4100), (64, 4096, 28672), (48, 4096, 28672), (57, 1024, 24576)])
+                                   (1024, 1024, 4100), (64, 4096, 28672), (48, 4096, 28672), (57, 1024, 24576),
+                                   (56, 1024, 57344), (49, 512, 57352)])
 def test_mid_m_problems_on_each_kernel(m, k, n, accum):
-    """Around the skinny kernel's bounds: problems too small for the
+    """Around the skinny kernels' bounds: problems too small for the
     matrix-core tiles (64 < M <= 256 and N * ceil(M / 64) < 20480) run on
     the skinny kernel in grid rows of 64 rows of M, as do M <= 64 but for
-    48 < M <= 64 with N >= 24576 (the widest weights); the skinny kernel
-    sums with fp32-class precision whatever the mode asked for (both modes
-    meet the fp32 bound and give the same bits).  The others run on the
-    matrix-core GEMM with 128 x 128 tiles (too few 256 x 256 ones to occupy
-    the GPU): M = 96 and 256 on N = 14336 and 6144, M = 320 and 1024 with
-    ragged N, M = 57 and 64 on N of 24576 and 28672."""
+    48 < M <= 64 with N >= 57344 (two rounds of 128 x 128 tiles and more);
+    the skinny kernels sum with fp32-class precision whatever the mode asked
+    for (both modes meet the fp32 bound and give the same bits).  The others
+    run on the matrix-core GEMM with 128 x 128 tiles (too few 256 x 256 ones
+    to occupy the GPU): M = 96 and 256 on N = 14336 and 6144, M = 320 and
+    1024 with ragged N, M = 56 and 49 on N of 57344 and more.  M = 48 to 64
+    on N of 24576 and 28672 run the wide skinny kernel."""
     say("mid m", m, k, n, accum)
     d = _prepare(7, m, k, n, per_channel=True, outliers=True, rowmul=True, with_bias=True)
-    skinny = (m <= 64 and not (m > 48 and n >= 24576)) or (64 < m <= 256 and n * ((m + 63) // 64) < 20480)
+    skinny = (m <= 64 and not (m > 48 and n >= 57344)) or (64 < m <= 256 and n * ((m + 63) // 64) < 20480)
     out = fp8.scaled_mm(d["a_q"], d["w_q"], d["s_a"], d["s_w"], True, d["bias"], accum=accum)
     torch.cuda.synchronize()
     ref = oracle.scaled_mm(d["aq"], d["wq"], d["sa"], d["sw"], True, d["bias_bits"])
