@@ -110,6 +110,8 @@ def test_mid_m(m, k, n):
     (24, 1040, 28680, False, True),   # a ragged k step (K = 4 x 256 + 16)
     (48, 4096, 28676, True, True),    # N % 8 == 4: 8-byte stores, the last columns element by element
     (63, 4096, 14339, True, True),    # odd N: every row of the last block element by element
+    (40, 16, 14400, True, True),      # one partial k step (K = 16): the pipeline's second slot never loads
+    (50, 272, 28672, True, True),     # one step and a 16-byte tail; 48 < M <= 64 below N = 57344
 ])
 def test_wide_skinny_kernel(m, k, n, pc, bias):
     """The wide skinny kernel (each wave its own 16-row weight block over all
