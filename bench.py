@@ -15,7 +15,7 @@ Workloads (synthetic, seeded; the models' shapes only -- no checkpoints):
   skinny   single per-tensor linears at small M: 16 x 4096 -> 4096, and
            Mistral-7B-shaped GEMMs at M in {1, 3, 7, 13} (and 32, 64) with
            N not a multiple of 16, weights rotated over >= 1 GiB per shape.
-  mid_m    the four Llama-3-8B GEMMs at M in {65, 128, 256, 512, 1024},
+  mid_m    the four Llama-3-8B GEMMs at M in {32, 64, 65, 128, 256, 512, 1024},
            between decode and prefill.
 
 The default run (--workload all) prints the decode line (the headline value
@@ -54,7 +54,7 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix throughput, published
 ROTATE_DECODE = 8
 ROTATE_MIN_BYTES = 1 << 30   # skinny GEMMs: weights rotated over at least this many bytes
 PREFILL_M = 16384
-MID_M = (65, 128, 256, 512, 1024)
+MID_M = (32, 64, 65, 128, 256, 512, 1024)
 
 
 def quant_bytes(m, k):
@@ -306,7 +306,7 @@ def bench_skinny(args):
 
 
 def bench_mid_m(args):
-    """GEMMs between decode and prefill: M in {65, 128, 256, 512, 1024} rows
+    """GEMMs between decode and prefill: M in {32, 64, 65, 128, 256, 512, 1024} rows
     on the Llama-3-8B shapes (channelwise scales, fp32-class sums), each
     weight rotated over copies totalling at least 1 GiB.  The call gives
     problems too small for the matrix-core tiles to the skinny kernel and
@@ -336,7 +336,7 @@ def bench_mid_m(args):
                          "rotation_copies": len(copies)})
         del copies, w_q
         torch.cuda.empty_cache()
-    return {"workload": "llama3-8b linears at M = 65, 128, 256, 512, 1024 (between decode and prefill), channelwise weight "
+    return {"workload": "llama3-8b linears at M = 32, 64, 65, 128, 256, 512, 1024 (between decode and prefill), channelwise weight "
                         "scales, fp32-class sums, weights rotated over >= 1 GiB per shape",
             "gemms": rows}
 
@@ -589,7 +589,7 @@ def main():
                     default="all",
                     help="all (default): the decode line with prefill (both accumulation modes) and skinny "
                          "objects added; decode / prefill: that workload alone as the headline; skinny: the "
-                         "small-M per-tensor GEMMs alone; mid_m: the GEMMs at M = 65 to 1024 alone; next: the "
+                         "small-M per-tensor GEMMs alone; mid_m: the GEMMs at M = 32 to 1024 alone; next: the "
                          "producer-fused, static and weight "
                          "quantizations and e5m2 GEMMs alone; chain: the 32-layer Llama-3-8B-shaped stack, "
                          "16 x 1024-token prefill, then decode steps at M=16 (--steps of them, default 512)")
