@@ -521,7 +521,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_mb_kernel(GemmArgs g) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r = lane & 15, grp = lane >> 4;
-  const int n0 = blockIdx.x * 16, m0 = blockIdx.y * (16 * MB);
+  // Workgroups are dealt to the 8 XCDs in dispatch order (x fastest).  The
+  // linear id is taken apart so that the grid rows of M of one weight block
+  // come 8 ids apart: the same XCD at about the same time, so the weight
+  // block streams from HBM once and that XCD's L2 serves the other rows.
+  const uint32_t tn = gridDim.x, tm = gridDim.y;
+  const uint32_t id = blockIdx.x + blockIdx.y * tn;
+  const uint32_t group = id / (8 * tm), rem = id - group * (8 * tm);
+  const uint32_t width = min(8u, tn - group * 8);  // weight blocks in this group
+  const int n0 = (int)(group * 8 + rem % width) * 16, m0 = (int)(rem / width) * (16 * MB);
   const int steps = (g.K + 255) >> 8;
   int first, stride, count;
   if constexpr (IL) {
