@@ -849,7 +849,14 @@ hipError_t launch_generic(const GemmArgs& g, dim3 grid, hipStream_t stream) {
 }
 
 // Rows of M per grid row of the multi-block kernel.
-int skinny_rows_per_grid_row(const GemmArgs& g) { return 16 * min((g.M + 15) / 16, kMaxSkinnyBlocks); }
+// The 16-row blocks of M are spread evenly over the ceil(M / 64) grid rows
+// (65 rows: two grid rows of 3 blocks, not 4 + 4), so no grid row runs
+// blocks that lie wholly past M.
+int skinny_rows_per_grid_row(const GemmArgs& g) {
+  const int blocks = (g.M + 15) / 16;
+  const int grid_rows = (blocks + kMaxSkinnyBlocks - 1) / kMaxSkinnyBlocks;
+  return 16 * ((blocks + grid_rows - 1) / grid_rows);
+}
 
 template <int MB, int FA, int FW>
 hipError_t launch_mb(const GemmArgs& g, hipStream_t stream) {
