@@ -52,16 +52,25 @@ fp8_status check_fmt(const char* fn, fp8_format f) {
 // Up to 256 rows the matrix-core GEMM has at most 2 ceil(N / 128) tiles of
 // 128 x 128 (one per CU at a time), so for N up to some 16k it runs a single
 // round of tiles whose time is proportional to K whatever M and N: about 36
-// us at K = 4096 with fp32-class sums, 29-31 us with fp8 sums.  The skinny
-// kernel reads the weight once per 64 rows of M instead, about 1.75 us per
-// 1024 of N ceil(M / 64) at K = 4096.  So the skinny kernel runs while
-// N ceil(M / 64) < 20480 (in both modes: 256 x 4096 -> 4096 took 28 us on
-// it against 31 us on the fp8 matrix cores).  Measured, 65-128 x 4096 ->
-// 4096 in 15-17 us and 65-128 x 14336 -> 4096 in 49-55 us on it, while
-// 65-128 x 4096 -> 14336 takes 49-52 us on it and 38-39 us on the
-// matrix-core GEMM.  The skinny kernel always sums with fp32-class
-// precision.
-bool few_tiles_for_matrix_cores(int64_t M, int64_t N) { return M <= 256 && N * ((M + 63) / 64) < 20480; }
+// us at K = 4096 with fp32-class sums, 29-33 us with fp8 sums.  The skinny
+// kernel reads the weight once per grid row of up to 64 rows of M, in time
+// about proportional to N and to the 16-row blocks each grid row carries
+// (the blocks of M are spread evenly over the ceil(M / 64) grid rows: 65 to
+// 96 rows run two rows of 3 blocks).  So the skinny kernel runs while
+// N x (grid rows x blocks per row) < 81920, in both modes (it always sums
+// with fp32-class precision).  Measured at K = 4096 and 14336 for N from
+// 4096 to 14336 and M from 65 to 256, with weights from HBM: every choice
+// within 2.1% of the faster kernel; 65-96 x 4096 -> 10240 on the skinny
+// kernel in 29-30 us against 37 us (fp32-class) and 32.5 us (fp8 sums) on
+// the matrix cores, 128 x 4096 -> 10240 (8 blocks) about even, 65 x 4096 ->
+// 14336 (6 blocks) 4-21% slower on it.
+int skinny_blocks_per_grid_row(int64_t M) {
+  const int64_t blocks = (M + 15) / 16, rows = (blocks + 3) / 4;
+  return (int)((blocks + rows - 1) / rows);
+}
+bool few_tiles_for_matrix_cores(int64_t M, int64_t N) {
+  return M <= 256 && N * ((M + 63) / 64) * skinny_blocks_per_grid_row(M) < 81920;
+}
 
 // From 17 to 64 rows the skinny kernels serve every block of 16 rows of M
 // from one weight step (on wide weights the wide variant, whose workgroups

@@ -181,7 +181,9 @@ fp8_status fp8_quant_dynamic_per_row(const uint16_t* x_bf16, int64_t rows, int64
  * few to occupy the GPU.
  * M <= 64 runs the skinny kernel, but for 48 < M <= 64 with N >= 57344.
  * Larger M runs the matrix-core GEMM, but for problems too small for its
- * tiles (M <= 256 and N * ceil(M / 64) below 20480).  Layouts the
+ * tiles: M <= 256 and N * R * B below 81920, where the skinny kernel runs
+ * R = ceil(M / 64) grid rows of B = ceil(ceil(M / 16) / R) blocks of 16
+ * rows.  Layouts the
  * matrix-core GEMM does not take (rows not 16-byte aligned or K % 16 != 0)
  * run the skinny kernel, which then reads the weight once per 64 rows of M
  * (per 16 rows for unaligned layouts).  Any M, N, K >= 1 is accepted.

@@ -176,11 +176,12 @@ def test_mfma_gemm(m, k, n, pc, accum):
 @pytest.mark.parametrize("m,k,n", [(65, 4096, 1030), (128, 4096, 4096), (256, 256, 256), (200, 14336, 300),
                                    (96, 4096, 8192), (96, 4096, 14336), (256, 4096, 6144), (320, 4096, 4096),
                                    (1024, 1024, 4100), (64, 4096, 28672), (48, 4096, 28672), (57, 1024, 24576),
-                                   (56, 1024, 57344), (49, 512, 57352)])
+                                   (56, 1024, 57344), (49, 512, 57352), (96, 1024, 10240), (128, 1024, 10240)])
 def test_mid_m_problems_on_each_kernel(m, k, n, accum):
     """Around the skinny kernels' bounds: problems too small for the
-    matrix-core tiles (64 < M <= 256 and N * ceil(M / 64) < 20480) run on
-    the skinny kernel in grid rows of 64 rows of M, as do M <= 64 but for
+    matrix-core tiles (64 < M <= 256 and N x the skinny kernel's 16-row block
+    slots below 81920: 96 x 10240 has 2 grid rows of 3, 128 x 10240 of 4)
+    run on the skinny kernel in grid rows of up to 64 rows of M, as do M <= 64 but for
     48 < M <= 64 with N >= 57344 (two rounds of 128 x 128 tiles and more);
     the skinny kernels sum with fp32-class precision whatever the mode asked
     for (both modes meet the fp32 bound and give the same bits).  The others
@@ -190,7 +191,10 @@ def test_mid_m_problems_on_each_kernel(m, k, n, accum):
     on N of 24576 and 28672 run the wide skinny kernel."""
     say("mid m", m, k, n, accum)
     d = _prepare(7, m, k, n, per_channel=True, outliers=True, rowmul=True, with_bias=True)
-    skinny = (m <= 64 and not (m > 48 and n >= 57344)) or (64 < m <= 256 and n * ((m + 63) // 64) < 20480)
+    blocks = (m + 15) // 16
+    rows = (blocks + 3) // 4
+    slots = rows * ((blocks + rows - 1) // rows)  # grid rows x blocks per grid row of the skinny kernel
+    skinny = (m <= 64 and not (m > 48 and n >= 57344)) or (64 < m <= 256 and n * slots < 81920)
     out = fp8.scaled_mm(d["a_q"], d["w_q"], d["s_a"], d["s_w"], True, d["bias"], accum=accum)
     torch.cuda.synchronize()
     ref = oracle.scaled_mm(d["aq"], d["wq"], d["sa"], d["sw"], True, d["bias_bits"])
