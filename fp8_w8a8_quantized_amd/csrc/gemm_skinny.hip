@@ -851,10 +851,19 @@ hipError_t launch_generic(const GemmArgs& g, dim3 grid, hipStream_t stream) {
 // Rows of M per grid row of the multi-block kernel.
 // The 16-row blocks of M are spread evenly over the ceil(M / 64) grid rows
 // (65 rows: two grid rows of 3 blocks, not 4 + 4), so no grid row runs
-// blocks that lie wholly past M.
+// blocks that lie wholly past M.  From 33 to 64 rows two grid rows of fewer
+// blocks replace one where a single row leaves the GPU short of workgroups:
+// N / 16 at most CUs / 2, or four blocks with N / 16 between CUs and
+// 2 x CUs.  (Per-channel GEMMs, weights from HBM, alternating runs: N = 1030
+// at M = 33-64 9.0-10.3 -> 7.1-7.4 us; N = 6144 at M = 56-64 16.3-16.8 ->
+// 14.0-14.6 us with K = 4096 and 48.2-48.8 -> 40.5-41.6 us with K = 14336;
+// elsewhere two rows lost up to 39%, e.g. K = 14336, N = 4096.)
 int skinny_rows_per_grid_row(const GemmArgs& g) {
   const int blocks = (g.M + 15) / 16;
-  const int grid_rows = (blocks + kMaxSkinnyBlocks - 1) / kMaxSkinnyBlocks;
+  int grid_rows = (blocks + kMaxSkinnyBlocks - 1) / kMaxSkinnyBlocks;
+  const int64_t wgs = ((int64_t)g.N + 15) / 16, cus = device_cus();
+  if (grid_rows == 1 && blocks > 2 && (wgs <= cus / 2 || (blocks == 4 && wgs > cus && wgs < 2 * cus)))
+    grid_rows = 2;
   return 16 * ((blocks + grid_rows - 1) / grid_rows);
 }
 

@@ -101,13 +101,18 @@ def test_mid_m(m, k, n):
     _run_and_check(d, False)
 
 
-@pytest.mark.parametrize("m,k,n", [(65, 1024, 4100), (81, 2048, 3000), (129, 1024, 4104), (190, 512, 2056)])
+@pytest.mark.parametrize("m,k,n", [(65, 1024, 4100), (81, 2048, 3000), (129, 1024, 4104), (190, 512, 2056),
+                                   (64, 2048, 6144), (50, 1024, 1030), (33, 512, 2040)])
 def test_skinny_grid_rows_share_the_blocks(m, k, n):
     """Past 64 rows the multi-block kernel runs ceil(M / 64) grid rows and
     spreads the 16-row blocks of M evenly over them: 65 and 81 rows as two
     grid rows of 3 blocks (the second with 1 and 33 rows), 129 as three of 3,
-    190 as three of 4; the grid rows of one weight block are dealt to one
-    XCD.  Per-channel scales, a bias, ragged N."""
+    190 as three of 4.  From 33 to 64 rows, on a 256-CU part, two grid rows
+    replace one where a single row has few workgroups: 64 x 6144 as two rows
+    of 2 blocks, 50 x 1030 as two of 2 (the second with 18 rows), 33 x 2040
+    (128 workgroups per row) as two of 2 (the second with 1 row).  The grid
+    rows of one weight block are dealt to one XCD.  Per-channel scales, a
+    bias, ragged N."""
     say("skinny grid rows", m, k, n)
     d = _prepare(10, m, k, n, per_channel=True, rowmul=True, with_bias=True, sub=m)
     _run_and_check(d, True)
