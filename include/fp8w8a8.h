@@ -183,10 +183,10 @@ fp8_status fp8_quant_dynamic_per_row(const uint16_t* x_bf16, int64_t rows, int64
  * Larger M runs the matrix-core GEMM, but for problems too small for its
  * tiles: M <= 256 and N * R * B below 81920, where the skinny kernel runs
  * R = ceil(M / 64) grid rows of B = ceil(ceil(M / 16) / R) blocks of 16
- * rows.  Layouts the
- * matrix-core GEMM does not take (rows not 16-byte aligned or K % 16 != 0)
- * run the skinny kernel, which then reads the weight once per 64 rows of M
- * (per 16 rows for unaligned layouts).  Any M, N, K >= 1 is accepted.
+ * rows.  Layouts the matrix-core GEMM does not take (rows not 16-byte
+ * aligned or K % 16 != 0) run the skinny kernel, which then reads the weight
+ * once per grid row of up to 64 rows of M (per 16 rows for unaligned
+ * layouts).  Any M, N, K >= 1 is accepted.
  * Errors: INVALID_ARG for null pointers (bias may be NULL), negative M or
  * N, K < 1, lda/ldw < K, ldo < N, or an unknown scale mode; UNSUPPORTED for
  * M or N >= 2^31, K >= 2^30 or pitches >= 2^40.  M == 0 or N == 0 is an
