@@ -91,11 +91,12 @@ def test_skinny_tiny_and_ragged_k(m, k, n):
                                    (40, 14336, 2401), (20, 4096, 8200), (48, 1040, 777), (63, 8208, 513),
                                    (57, 4096, 16)])
 def test_mid_m(m, k, n):
-    """16 < M <= 64 on the skinny kernel, every 16-row block of M in one
-    workgroup (two, three or four blocks); shapes with at least 32 MiB of
-    weights (non-temporal loads), interleaved and contiguous K steps, K
-    tails that are not whole 256-byte steps, a ragged N and a partial last
-    block of M."""
+    """16 < M <= 64 on the multi-block skinny kernel: two, three or four
+    16-row blocks of M per workgroup in one grid row, or two grid rows of 2
+    blocks where one row would have few workgroups (N <= 2048 here); shapes
+    with at least 32 MiB of weights (non-temporal loads), interleaved and
+    contiguous K steps, K tails that are not whole 256-byte steps, a ragged
+    N and a partial last block of M."""
     say("mid m", m, k, n)
     d = _prepare(4, m, k, n, per_channel=False, with_bias=True)
     _run_and_check(d, False)
@@ -186,8 +187,9 @@ def test_mid_m_problems_on_each_kernel(m, k, n, accum):
     """Around the skinny kernels' bounds: problems too small for the
     matrix-core tiles (64 < M <= 256 and N x the skinny kernel's 16-row block
     slots below 81920: 96 x 10240 has 2 grid rows of 3, 128 x 10240 of 4)
-    run on the skinny kernel in grid rows of up to 64 rows of M, as do M <= 64 but for
-    48 < M <= 64 with N >= 57344 (two rounds of 128 x 128 tiles and more);
+    run on the skinny kernel in grid rows of up to 64 rows of M, as do
+    M <= 64 but for 48 < M <= 64 with N >= 57344 (two rounds of 128 x 128
+    tiles and more);
     the skinny kernels sum with fp32-class precision whatever the mode asked
     for (both modes meet the fp32 bound and give the same bits).  The others
     run on the matrix-core GEMM with 128 x 128 tiles (too few 256 x 256 ones
@@ -234,8 +236,9 @@ def test_mfma_gemm_k_not_multiple_of_128(accum):
 def test_m_above_64_with_a_weight_pitch_the_matrix_core_kernel_refuses():
     """M = 80 with W rows 2^23 + 16 bytes apart: a 256-row weight panel would
     span 2 GiB, past the matrix-core kernel's 32-bit buffer offsets, so the
-    multi-block skinny kernel runs M in two grid rows of 64 (the second one
-    partly past M).  Only the first K bytes of each weight row are codes."""
+    multi-block skinny kernel runs M in two grid rows of 3 blocks of 16 rows
+    (the second one partly past M).  Only the first K bytes of each weight
+    row are codes."""
     m, k, n, ldw = 80, 4096, 24, (1 << 23) + 16
     say("pitched weight, M > 64", m, k, n, ldw)
     d = _prepare(9, m, k, n, per_channel=True, outliers=True, rowmul=True, with_bias=True)
