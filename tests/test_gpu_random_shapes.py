@@ -3,12 +3,16 @@
 Each case draws M, N, K, the row pitches of both operands and of the output,
 the scale mode, a bias, the operand formats and the accumulation mode from a
 fixed seed. Together the cases cross every dispatch path of the library:
-- the one- and two-block skinny kernels (M <= 16);
-- the multi-block skinny kernel (16 < M <= 64);
+- the one-block skinny kernel (M <= 16);
+- the multi-block skinny kernel (16 < M <= 64, in one or two grid rows);
 - the byte-granular kernel (K % 16 != 0 or unaligned pitches);
 - the matrix-core kernel (M > 64 with enough output tiles), with vector and
   2-byte output stores, and the multi-block skinny kernel for the 64 < M <= 256
-  problems too small for its tiles.
+  problems too small for its tiles;
+- on wide weights (N of 14305 and more, the last six cases, on a 256-CU
+  part): the two-block skinny kernel (M <= 16) and the wide skinny kernel
+  (16 < M <= 64), or the multi-block or byte-granular one where those do not
+  apply.
 The operands are quantized from the seeded generators on each side
 independently, and the GPU's codes must equal the oracle's byte for byte.
 """
@@ -47,6 +51,28 @@ def _cases(n_cases=30, seed=20261202):
     return out
 
 
+def _wide_cases(n_cases=6, seed=20261203):
+    """Wide weights with short K (so the oracle stays quick): M <= 16, 17-32
+    on N >= 28672, and 33-64 on N >= 14336."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for j in range(n_cases):
+        band = j % 3
+        m = int(rng.integers(1, 17) if band == 0 else rng.integers(17, 33) if band == 1 else rng.integers(33, 65))
+        lo = 28672 if band == 1 else 14305
+        n = int(rng.integers(lo, 32001))
+        aligned = rng.random() < 0.8
+        k = int(rng.integers(1, 33) * 16 if aligned else rng.integers(1, 520))
+        pad_a = int(rng.choice([0, 16, 48]))
+        pad_w = int(rng.choice([0, 32, 7]))
+        pad_o = int(rng.choice([0, 8, 3]))
+        per_channel = bool(rng.random() < 0.6)
+        with_bias = bool(rng.random() < 0.5)
+        fmt_a, fmt_w = [("e4m3", "e4m3"), ("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2")][int(rng.integers(0, 4))]
+        out.append((30 + j, m, n, k, pad_a, pad_w, pad_o, per_channel, with_bias, fmt_a, fmt_w, "fp32"))
+    return out
+
+
 def _pitched_codes(codes, pad):
     """A device uint8 view [rows, cols] inside a [rows, cols + pad] buffer."""
     rows, cols = codes.shape
@@ -56,7 +82,7 @@ def _pitched_codes(codes, pad):
     return view
 
 
-@pytest.mark.parametrize("case", _cases(), ids=lambda c: f"c{c[0]}-m{c[1]}-n{c[2]}-k{c[3]}")
+@pytest.mark.parametrize("case", _cases() + _wide_cases(), ids=lambda c: f"c{c[0]}-m{c[1]}-n{c[2]}-k{c[3]}")
 def test_random_problem(case):
     i, m, n, k, pad_a, pad_w, pad_o, per_channel, with_bias, fmt_a, fmt_w, accum = case
     say("random gemm", case)
