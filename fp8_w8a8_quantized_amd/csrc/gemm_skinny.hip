@@ -40,13 +40,16 @@
 // every 16-row block of M (up to four) from each weight step, so the weight
 // still streams once; larger M on this path (problems of up to 256 rows too
 // small for the matrix-core GEMM's tiles, and layouts that kernel does not
-// take) uses grid rows of 64.  On wide weights, M from 17 to 64 runs a wide
-// variant instead: each wave owns a weight block over the whole of K and the
-// workgroup loads each activation step once for its four blocks, so fewer
-// activation lines pass the texture path per weight line.  Layouts that are not 16-byte
-// aligned (or K % 16 != 0) use a byte-granular variant that loads each
-// lane's 32 bytes directly in the matrix-core layout, one 16-row block of M
-// per grid row.
+// take) runs ceil(M / 64) grid rows with the blocks spread evenly over them,
+// and the grid rows of one weight block share an XCD, whose L2 serves the
+// repeated weight reads (so do two grid rows of fewer blocks, which replace
+// one where a single row would have few workgroups).  On wide weights, M
+// from 17 to 64 runs a wide variant instead: each wave owns a weight block
+// over the whole of K and the workgroup loads each activation step once for
+// its four blocks, so fewer activation lines pass the texture path per
+// weight line.  Layouts that are not 16-byte aligned (or K % 16 != 0) use a
+// byte-granular variant that loads each lane's 32 bytes directly in the
+// matrix-core layout, one 16-row block of M per grid row.
 
 #include <algorithm>
 #include <atomic>
